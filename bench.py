@@ -1,0 +1,179 @@
+"""Throughput of the S6 selective scan (forward + backward) on one MI355X.
+
+One step = ssm_scan_fwd (training, writes checkpoints) + ssm_scan_bwd over one
+batch of the Mamba-2.8B-shaped workload: batch 4, seqlen 8192, d_inner 5120,
+d_state 16, bf16 activations, f32 state and arithmetic.  Inputs are seeded
+synthetic tensors already resident in HBM.  The metric is elements
+(batch*seqlen*d_inner*d_state) per second.
+
+Prints ONE JSON line.  Besides the contract fields it carries
+  roofline      : the dominant kernel's algorithmic bytes per launch / its
+                  average launch time (HIP events recorded by the library around
+                  each launch on the launch stream), against 8 TB/s HBM;
+  cpu_baseline  : the f64 oracle timed on a bounded sample on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c4_mamba2p8b_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=2,
+                    help="batch rows the oracle baseline runs on (all tokens)")
+    ap.add_argument("--cpu-sample-channels", type=int, default=0,
+                    help="channels the oracle baseline runs on (0 = all)")
+    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg, esz):
+    """Compulsory bytes: every input read once, every output written once."""
+    b, L, d, n = cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"]
+    btd, btn = b * L * d, b * L * n
+    params = 4 * (d * n + 2 * d)
+    fwd = btd * esz * 4 + btn * esz * 2 + params          # x, dt, z in; y out; B, C in
+    bwd_main = btd * esz * 7 + btn * esz * 2 + params     # x, dt, z, dy in; dx, ddt, dz out; B, C in
+    bwd = bwd_main + btn * esz * 2 + params               # + dB, dC, param grads out
+    return {"fwd": fwd, "bwd": bwd, "bwd_main": bwd_main, "fwd_main": fwd}
+
+
+def cpu_baseline(inp, cfg, rows, channels):
+    import numpy as np
+
+    import oracle
+    dsel = slice(0, channels)
+    sub = {k: np.ascontiguousarray(inp[k][:rows, :, dsel]) for k in ("x", "z", "dt", "dy")}
+    sub.update({k: np.ascontiguousarray(inp[k][:rows]) for k in ("B", "C")})
+    sub.update({"A_log": inp["A_log"][dsel], "D": inp["D"][dsel], "dt_bias": inp["dt_bias"][dsel]})
+    sub = {k: v.astype(np.float64) for k, v in sub.items()}
+    t0 = time.perf_counter()
+    oracle.fwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"], sub["A_log"], sub["D"], sub["dt_bias"])
+    oracle.bwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"], sub["A_log"], sub["D"], sub["dt_bias"],
+               sub["dy"])
+    sec = time.perf_counter() - t0
+    elems = rows * cfg["seqlen"] * channels * cfg["d_state"]
+    return {"value": elems / sec, "unit": "elements/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"batch rows 0..{rows - 1}, all {cfg['seqlen']} tokens, channels 0..{channels - 1} of "
+                      f"the same workload, fwd+bwd in f64 ({elems} elements, {sec:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the scan is measured on a "
+              f"single MI355X and multi-GPU sharding is design-only.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import selective_state_space_04_amd as ssm
+    import workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    if "bwd" not in cfg["passes"]:
+        raise SystemExit(f"{args.config} is not a fwd+bwd workload")
+    dev = torch.device("cuda:0")
+    io = torch.bfloat16 if cfg["io"] == "bf16" else torch.float32
+    esz = 2 if io == torch.bfloat16 else 4
+    print(f"[bench] generating {args.config} inputs", file=sys.stderr, flush=True)
+    inp = W.make_config(args.config)
+    t = {}
+    for k in ("x", "z", "dt", "B", "C", "dy"):
+        t[k] = torch.from_numpy(inp[k]).to(dev).to(io)
+    for k in ("A_log", "D", "dt_bias"):
+        t[k] = torch.from_numpy(inp[k]).to(dev)
+    bsz, L, D = inp["x"].shape
+    N = cfg["d_state"]
+    grads = {"dx": torch.empty_like(t["x"]), "ddt": torch.empty_like(t["x"]), "dz": torch.empty_like(t["x"]),
+             "dB": torch.empty_like(t["B"]), "dC": torch.empty_like(t["C"]),
+             "dA_log": torch.empty_like(t["A_log"]), "dD": torch.empty_like(t["D"]),
+             "ddt_bias": torch.empty_like(t["dt_bias"]), "dh0": None}
+    y = torch.empty_like(t["x"])
+
+    def step(timer=None):
+        _, _, ckpt = ssm.ssm_scan_fwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"],
+                                      t["dt_bias"], training=True, y=y, timing=timer)
+        ssm.ssm_scan_bwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"], ckpt,
+                         t["dy"], out=grads, timing=timer)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [ssm.LaunchTimer() for _ in range(args.steps)]
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(timers[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per_kernel = {}
+    for tm in timers:
+        for name, kms in tm.results():
+            per_kernel.setdefault(name, []).append(kms)
+    for tm in timers:
+        tm.close()
+    kavg = {k: float(np.mean(v)) for k, v in per_kernel.items()}
+    kcount = {k: len(v) // args.steps for k, v in per_kernel.items()}
+    dominant = max(kavg, key=lambda k: kavg[k] * kcount[k])
+    ab = algorithmic_bytes(cfg, esz)
+    dom_bytes = {"k_bwd_main": ab["bwd_main"], "k_fwd_main": ab["fwd_main"]}.get(dominant)
+    elems = bsz * L * D * N
+    roof = None
+    if dom_bytes is not None:
+        achieved = dom_bytes / (kavg[dominant] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dominant,
+                "kernel_ms": round(kavg[dominant], 4), "algorithmic_bytes_per_launch": dom_bytes}
+    line = {
+        "metric": "selective-scan fwd+bwd elements(B\u00b7L\u00b7D\u00b7N)/s and achieved HBM GB/s",
+        "value": elems / (ms * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: batch={bsz} seqlen={L} d_inner={D} d_state={N}, "
+                               f"{cfg['io']} activations, f32 state, fwd+bwd",
+                   "batch": bsz, "seqlen": L, "d_inner": D, "d_state": N, "io_dtype": cfg["io"]},
+        "achieved_hbm_GBps": round((ab["fwd"] + ab["bwd"]) / (ms * 1e-3) / 1e9, 1),
+        "kernels_ms": {k: round(v, 4) for k, v in sorted(kavg.items())},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        ch = args.cpu_sample_channels or D
+        line["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_rows, bsz), min(ch, D))
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()

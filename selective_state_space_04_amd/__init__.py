@@ -1,0 +1,300 @@
+"""MI355X-native Mamba S6 selective scan.
+
+Thin Python binding of ``libssmscan.so`` (built from ``csrc/ssm_scan.hip``): it
+checks tensors, allocates outputs/workspace through torch's caching allocator
+and passes raw device pointers and the current HIP stream to the C ABI declared
+in ``include/ssm_scan.h``.  Every step of the scan runs in the library's HIP
+kernels; there is no other code path.  Importing fails loudly when the library
+has not been built (``__graft_entry__.build()``).
+
+Operation (rustytorch commit log, page "crates/training/rtx-transformers/tests",
+commits introducing the real S6 forward, its hand-written VJP and
+MambaRecurrence::step):
+    delta = softplus(dt + dt_bias), A = -exp(A_log)
+    h_t   = exp(delta*A) h_{t-1} + delta B_t x_t,   y_t = (C_t.h_t + D x_t) silu(z_t)
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+D_STATE = 16
+TIMING_MAX = 16
+
+
+class SsmDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("d_inner", ctypes.c_int64), ("d_state", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32)]
+
+
+class SsmTiming(ctypes.Structure):
+    _fields_ = [("events", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("count", ctypes.c_int32), ("kernel_id", ctypes.c_int32 * TIMING_MAX)]
+
+
+class SsmError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first (python -c "
+            f"'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    DP = ctypes.POINTER(SsmDims)
+    TP = ctypes.POINTER(SsmTiming)
+    lib.ssm_status_str.argtypes = [ctypes.c_int]
+    lib.ssm_status_str.restype = ctypes.c_char_p
+    lib.ssm_kernel_name.argtypes = [I32]
+    lib.ssm_kernel_name.restype = ctypes.c_char_p
+    for fn in ("ssm_scan_ckpt_bytes", "ssm_scan_fwd_workspace_bytes", "ssm_scan_bwd_workspace_bytes"):
+        getattr(lib, fn).argtypes = [DP]
+        getattr(lib, fn).restype = SZ
+    lib.ssm_scan_fwd.argtypes = [DP] + [P] * 12 + [P, SZ, P, TP]
+    lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_bwd.argtypes = [DP] + [P] * 20 + [P, SZ, P, TP]
+    lib.ssm_scan_bwd.restype = ctypes.c_int
+    lib.ssm_scan_step.argtypes = [I64, I64, I64, I32] + [P] * 10 + [P, TP]
+    lib.ssm_scan_step.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load_library()
+
+
+def library():
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def status_str(code):
+    return _lib.ssm_status_str(int(code)).decode()
+
+
+def kernel_name(kid):
+    return _lib.ssm_kernel_name(int(kid)).decode()
+
+
+def _raise(fn, code):
+    if code != 0:
+        raise SsmError(fn, code, status_str(code))
+
+
+def _io_code(dtype):
+    if dtype == torch.float32:
+        return SSM_F32
+    if dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"unsupported io dtype {dtype}: use float32 or bfloat16")
+
+
+def dims(batch, seqlen, d_inner, d_state=D_STATE, io_dtype=torch.float32):
+    return SsmDims(int(batch), int(seqlen), int(d_inner), int(d_state), _io_code(io_dtype))
+
+
+def ckpt_bytes(batch, seqlen, d_inner, d_state=D_STATE, io_dtype=torch.float32):
+    return int(_lib.ssm_scan_ckpt_bytes(ctypes.byref(dims(batch, seqlen, d_inner, d_state, io_dtype))))
+
+
+def fwd_workspace_bytes(batch, seqlen, d_inner, d_state=D_STATE, io_dtype=torch.float32):
+    return int(_lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(dims(batch, seqlen, d_inner, d_state, io_dtype))))
+
+
+def bwd_workspace_bytes(batch, seqlen, d_inner, d_state=D_STATE, io_dtype=torch.float32):
+    return int(_lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(dims(batch, seqlen, d_inner, d_state, io_dtype))))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device, required=True):
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    # dense row-major only: strides are never interpreted
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (dense row-major)")
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _timing_ptr(timing):
+    return None if timing is None else ctypes.byref(timing.struct)
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def ssm_scan_fwd(x, dt, B, C, z, A_log, D, dt_bias, h0=None, *, training=False,
+                 return_last_state=False, y=None, stream=None, timing=None):
+    """Forward scan.  x, dt, z: [batch, L, d_inner]; B, C: [batch, L, 16] (float32 or
+    bfloat16, all the same); A_log [d_inner, 16], D, dt_bias [d_inner] float32; h0
+    [batch, d_inner, 16] float32 or None.  Returns (y, h_last or None, ckpt or None);
+    ckpt (training=True) is what ssm_scan_bwd needs."""
+    dev = x.device
+    bsz, L, din = x.shape
+    io = x.dtype
+    _check(x, "x", (bsz, L, din), io, dev)
+    _check(dt, "dt", (bsz, L, din), io, dev)
+    _check(B, "B", (bsz, L, D_STATE), io, dev)
+    _check(C, "C", (bsz, L, D_STATE), io, dev)
+    _check(z, "z", (bsz, L, din), io, dev, required=False)
+    _check(A_log, "A_log", (din, D_STATE), torch.float32, dev)
+    _check(D, "D", (din,), torch.float32, dev, required=False)
+    _check(dt_bias, "dt_bias", (din,), torch.float32, dev, required=False)
+    _check(h0, "h0", (bsz, din, D_STATE), torch.float32, dev, required=False)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (bsz, L, din), io, dev)
+    dm = dims(bsz, L, din, D_STATE, io)
+    h_last = torch.empty(bsz, din, D_STATE, dtype=torch.float32, device=dev) if return_last_state else None
+    ckpt = None
+    if training:
+        ckpt = torch.empty(_lib.ssm_scan_ckpt_bytes(ctypes.byref(dm)) // 4, dtype=torch.float32, device=dev)
+    nws = _lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(dm))
+    ws = _workspace(nws, dev)
+    rc = _lib.ssm_scan_fwd(ctypes.byref(dm), _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(z), _ptr(A_log),
+                           _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_last), _ptr(ckpt),
+                           _ptr(ws), nws, _stream(dev, stream), _timing_ptr(timing))
+    _raise("ssm_scan_fwd", rc)
+    return y, h_last, ckpt
+
+
+def ssm_scan_bwd(x, dt, B, C, z, A_log, D, dt_bias, ckpt, dy, h0=None, *, want_dh0=False,
+                 stream=None, timing=None, out=None):
+    """Backward of ssm_scan_fwd for the loss sum(dy * y).  Returns a dict with dx, ddt,
+    dz (None without z), dB, dC (io dtype) and dA_log, dD, ddt_bias, dh0 (float32)."""
+    dev = x.device
+    bsz, L, din = x.shape
+    io = x.dtype
+    for t, n, shp in ((x, "x", (bsz, L, din)), (dt, "dt", (bsz, L, din)), (B, "B", (bsz, L, D_STATE)),
+                      (C, "C", (bsz, L, D_STATE)), (dy, "dy", (bsz, L, din))):
+        _check(t, n, shp, io, dev)
+    _check(z, "z", (bsz, L, din), io, dev, required=False)
+    _check(A_log, "A_log", (din, D_STATE), torch.float32, dev)
+    _check(D, "D", (din,), torch.float32, dev, required=False)
+    _check(dt_bias, "dt_bias", (din,), torch.float32, dev, required=False)
+    _check(h0, "h0", (bsz, din, D_STATE), torch.float32, dev, required=False)
+    dm = dims(bsz, L, din, D_STATE, io)
+    nck = _lib.ssm_scan_ckpt_bytes(ctypes.byref(dm)) // 4
+    _check(ckpt, "ckpt", (nck,), torch.float32, dev)
+    g = out if out is not None else {}
+    g.setdefault("dx", torch.empty_like(x))
+    g.setdefault("ddt", torch.empty_like(x))
+    g.setdefault("dz", torch.empty_like(x) if z is not None else None)
+    g.setdefault("dB", torch.empty_like(B))
+    g.setdefault("dC", torch.empty_like(C))
+    g.setdefault("dA_log", torch.empty_like(A_log))
+    g.setdefault("dD", torch.empty(din, dtype=torch.float32, device=dev))
+    g.setdefault("ddt_bias", torch.empty(din, dtype=torch.float32, device=dev))
+    g.setdefault("dh0", torch.empty(bsz, din, D_STATE, dtype=torch.float32, device=dev) if want_dh0 else None)
+    nws = _lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(dm))
+    ws = _workspace(nws, dev)
+    rc = _lib.ssm_scan_bwd(ctypes.byref(dm), _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(z), _ptr(A_log),
+                           _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(ckpt), _ptr(dy), _ptr(g["dx"]),
+                           _ptr(g["ddt"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dz"]), _ptr(g["dA_log"]),
+                           _ptr(g["dD"]), _ptr(g["ddt_bias"]), _ptr(g["dh0"]), _ptr(ws), nws,
+                           _stream(dev, stream), _timing_ptr(timing))
+    _raise("ssm_scan_bwd", rc)
+    return g
+
+
+def ssm_scan_step(h, x, dt, B, C, z, A_log, D, dt_bias, *, y=None, stream=None, timing=None):
+    """One token: h [batch, d_inner, 16] float32 is updated in place; x, dt, z
+    [batch, d_inner] and B, C [batch, 16] in the io dtype.  Returns y [batch, d_inner]."""
+    dev = x.device
+    bsz, din = x.shape
+    io = x.dtype
+    _check(h, "h", (bsz, din, D_STATE), torch.float32, dev)
+    _check(x, "x", (bsz, din), io, dev)
+    _check(dt, "dt", (bsz, din), io, dev)
+    _check(B, "B", (bsz, D_STATE), io, dev)
+    _check(C, "C", (bsz, D_STATE), io, dev)
+    _check(z, "z", (bsz, din), io, dev, required=False)
+    _check(A_log, "A_log", (din, D_STATE), torch.float32, dev)
+    _check(D, "D", (din,), torch.float32, dev, required=False)
+    _check(dt_bias, "dt_bias", (din,), torch.float32, dev, required=False)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (bsz, din), io, dev)
+    rc = _lib.ssm_scan_step(bsz, din, D_STATE, _io_code(io), _ptr(h), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                            _ptr(z), _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(y), _stream(dev, stream),
+                            _timing_ptr(timing))
+    _raise("ssm_scan_step", rc)
+    return y
+
+
+class LaunchTimer:
+    """Per-kernel timing through the ABI's optional launch log: HIP events recorded
+    by the library around each of its launches, on the launch stream."""
+
+    def __init__(self, capacity=TIMING_MAX):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.capacity = min(capacity, TIMING_MAX)
+        self._events = (ctypes.c_void_p * (2 * self.capacity))()
+        for i in range(2 * self.capacity):
+            ev = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self._events[i] = ev
+        self.struct = SsmTiming()
+        self.struct.events = ctypes.cast(self._events, ctypes.c_void_p)
+        self.struct.capacity = self.capacity
+        self.reset()
+
+    def reset(self):
+        self.struct.count = 0
+
+    def results(self):
+        """[(kernel name, milliseconds)] for the recorded launches (call after a sync)."""
+        out = []
+        for i in range(self.struct.count):
+            ms = ctypes.c_float()
+            rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self._events[2 * i], self._events[2 * i + 1])
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            out.append((kernel_name(self.struct.kernel_id[i]), ms.value))
+        return out
+
+    def close(self):
+        for i in range(2 * self.capacity):
+            if self._events[i]:
+                self._hip.hipEventDestroy(self._events[i])
+                self._events[i] = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+__all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_scan_step", "ckpt_bytes", "fwd_workspace_bytes",
+           "bwd_workspace_bytes", "LaunchTimer", "SsmError", "library", "status_str", "kernel_name",
+           "SsmDims", "SsmTiming"]

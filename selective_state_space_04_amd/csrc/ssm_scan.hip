@@ -1,0 +1,921 @@
+// ssm_scan.hip -- Mamba S6 selective scan for MI355X (gfx950, CDNA4, wave64).
+//
+// Operation (rustytorch commit log, page "crates/training/rtx-transformers/tests",
+// commit replacing the MambaBlock stub with a real S6 forward):
+//   delta = softplus(dt + dt_bias), A = -exp(A_log)
+//   h_t   = exp(delta*A) * h_{t-1} + delta*B_t*x_t        (per batch, channel, state)
+//   y_t   = (sum_n C_t[n] h_t[n] + D x_t) * silu(z_t)
+// Backward: the reverse-time adjoint (commit adding the hand-written VJP),
+// dA_log = dA * A, parameter gradients summed over batch and time.
+// Step: the forward's per-token body on a carried state (commit introducing
+// MambaRecurrence::step); it shares scan_token()/finish_y() with the forward so
+// that stepping reproduces a single-chunk forward bit for bit.
+//
+// Mapping to the hardware
+//   * One lane owns one (batch, channel) and its 16 states in VGPRs.  A
+//     workgroup is 256 consecutive channels of one batch row, so x/dt/z/y are
+//     coalesced per token and B_t/C_t (shared by all channels) are
+//     wave-uniform loads served by the scalar cache.
+//   * Long sequences are cut into K chunks so that batch*d_inner*K lanes fill
+//     the 256 CUs.  Forward: (1) each chunk's zero-start end state S and delta
+//     sum; (2) a sequential combine h <- exp(A*sum delta)*h + S over chunks
+//     gives every chunk's true start; (3) every chunk re-runs from its start and
+//     writes y and the checkpoints.  The backward mirrors this with the adjoint
+//     (lambda <- exp(A*sum delta)*lambda + G, walking chunks in reverse).
+//   * The backward recomputes states from checkpoints taken every TS tokens,
+//     keeps the TS+1 states of a block in registers and sweeps it in reverse.
+//   * dB/dC (sums over channels) are reduced through LDS per wave, across the
+//     4 waves per block, then across workgroups by a fixed-order kernel: no
+//     atomics, bitwise deterministic.
+//   * exp(delta*A) is one v_exp_f32 of delta*(A*log2 e).  No MFMA: nothing on
+//     this path is a dense contraction.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "ssm_scan.h"
+
+namespace {
+
+constexpr int NS = 16;    // d_state handled by these kernels
+constexpr int TS = 8;     // checkpoint stride (tokens)
+constexpr int WG = 256;   // threads per workgroup: one channel each
+constexpr int NWAVE = WG / 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr int64_t TARGET_LANES = 262144;  // 4096 waves = 4 per SIMD
+constexpr int64_t MIN_CHUNK = 64;
+
+typedef uint16_t bf16_t;
+
+// ------------------------------------------------------------------ io helpers
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);                                           // nearest even
+    return (bf16_t)(u >> 16);
+}
+
+// 16 consecutive values (one B_t or C_t row); the address is wave-uniform.
+__device__ __forceinline__ void load16(const float* __restrict__ p, float v[NS]) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float4 f = q[i];
+        v[4 * i + 0] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+}
+__device__ __forceinline__ void load16(const bf16_t* __restrict__ p, float v[NS]) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        uint4 u = q[i];
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
+            v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ void load_state(const float* __restrict__ p, float h[NS]) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float4 f = q[i];
+        h[4 * i + 0] = f.x; h[4 * i + 1] = f.y; h[4 * i + 2] = f.z; h[4 * i + 3] = f.w;
+    }
+}
+__device__ __forceinline__ void store_state(float* __restrict__ p, const float h[NS]) {
+    float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = make_float4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+}
+
+// ---------------------------------------------------------------- token math
+// A2[n] = A[n] * log2(e) with A = -exp(A_log), so exp(delta*A) = exp2(delta*A2).
+__device__ __forceinline__ void load_A2(const float* __restrict__ A_log, int d, float A2[NS]) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) A2[n] = -expf(A_log[(int64_t)d * NS + n]) * LOG2E;
+}
+
+// Stable softplus(u) = max(u,0) + log1p(exp(-|u|)); also returns sigmoid(u),
+// its derivative.
+__device__ __forceinline__ float softplus_sig(float u, float& sig) {
+    float e = __expf(-fabsf(u));
+    float r = __builtin_amdgcn_rcpf(1.0f + e);
+    sig = u >= 0.0f ? r : e * r;
+    return fmaxf(u, 0.0f) + log1pf(e);
+}
+
+__device__ __forceinline__ float sigmoid_f(float z) {
+    float e = __expf(-fabsf(z));
+    float r = __builtin_amdgcn_rcpf(1.0f + e);
+    return z >= 0.0f ? r : e * r;
+}
+
+// One token of the recurrence for one channel: h <- exp2(delta*A2) h + (delta x) B,
+// returns sum_n C[n] h[n] (accumulated in state order).
+__device__ __forceinline__ float scan_token(float h[NS], const float A2[NS], const float Bv[NS],
+                                            const float Cv[NS], float delta, float xv) {
+    const float dxv = delta * xv;
+    float acc = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        const float a = __builtin_amdgcn_exp2f(delta * A2[n]);
+        h[n] = __builtin_fmaf(a, h[n], dxv * Bv[n]);
+        acc = __builtin_fmaf(Cv[n], h[n], acc);
+    }
+    return acc;
+}
+
+template <bool GATE>
+__device__ __forceinline__ float finish_y(float acc, float Dd, float xv, float zv) {
+    const float ypre = __builtin_fmaf(Dd, xv, acc);
+    if (!GATE) return ypre;
+    return ypre * (zv * sigmoid_f(zv));
+}
+
+// ===================================================================== forward
+
+// (1) zero-start end state S and delta sum of chunk k (k = 0 .. K-2).
+template <typename T>
+__global__ __launch_bounds__(WG) void k_fwd_chunk(
+    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    float* __restrict__ wsS, float* __restrict__ wsSum, int L, int D, int Tc, int K) {
+    const int d = blockIdx.x * WG + threadIdx.x;
+    const int k = blockIdx.y;
+    const int b = blockIdx.z;
+    const bool act = d < D;
+    const int dc = act ? d : D - 1;
+    float A2[NS];
+    load_A2(A_log, dc, A2);
+    const float bias = dt_bias ? dt_bias[dc] : 0.0f;
+    float S[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) S[n] = 0.0f;
+    float sumd = 0.0f;
+    const int t0 = k * Tc, t1 = min(t0 + Tc, L);
+    const int64_t row0 = (int64_t)b * L + t0;
+    const T* xp = x + row0 * D + dc;
+    const T* dp = dt + row0 * D + dc;
+    const T* bp = Bm + row0 * NS;
+    for (int t = t0; t < t1; ++t, xp += D, dp += D, bp += NS) {
+        const float xv = to_f(*xp), dtv = to_f(*dp);
+        float Bv[NS];
+        load16(bp, Bv);
+        float sg;
+        const float delta = softplus_sig(dtv + bias, sg);
+        const float dxv = delta * xv;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const float a = __builtin_amdgcn_exp2f(delta * A2[n]);
+            S[n] = __builtin_fmaf(a, S[n], dxv * Bv[n]);
+        }
+        sumd += delta;
+    }
+    if (act) {
+        const int64_t e = ((int64_t)b * (K - 1) + k) * D + d;
+        store_state(wsS + e * NS, S);
+        wsSum[e] = sumd;
+    }
+}
+
+// (2) chunk start states: starts(b, k) for k = 0..K-1, sequential over chunks.
+__global__ __launch_bounds__(WG) void k_fwd_carry(
+    const float* __restrict__ A_log, const float* __restrict__ h0, const float* __restrict__ wsS,
+    const float* __restrict__ wsSum, float* __restrict__ starts, int D, int K,
+    int64_t start_nent, int64_t start_kstep) {
+    const int d = blockIdx.x * WG + threadIdx.x;
+    const int b = blockIdx.z;
+    if (d >= D) return;
+    float A2[NS];
+    load_A2(A_log, d, A2);
+    float h[NS];
+    if (h0) load_state(h0 + ((int64_t)b * D + d) * NS, h);
+    else {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+    }
+    for (int k = 0; k < K; ++k) {
+        store_state(starts + (((int64_t)b * start_nent + (int64_t)k * start_kstep) * D + d) * NS, h);
+        if (k == K - 1) break;
+        const int64_t e = ((int64_t)b * (K - 1) + k) * D + d;
+        float S[NS];
+        load_state(wsS + e * NS, S);
+        const float sumd = wsSum[e];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const float P = __builtin_amdgcn_exp2f(A2[n] * sumd);
+            h[n] = __builtin_fmaf(P, h[n], S[n]);
+        }
+    }
+}
+
+// (3) recurrence of chunk k from its start; writes y, checkpoints and h_last.
+template <typename T, bool GATE>
+__global__ __launch_bounds__(WG) void k_fwd_main(
+    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
+    const T* __restrict__ Cm, const T* __restrict__ z, const float* __restrict__ A_log,
+    const float* __restrict__ Dp, const float* __restrict__ dt_bias,
+    const float* __restrict__ h0, const float* __restrict__ starts, T* __restrict__ y,
+    float* __restrict__ h_last, float* __restrict__ ckpt, int L, int D, int Tc, int K,
+    int64_t nck, int64_t start_nent, int64_t start_kstep) {
+    const int d = blockIdx.x * WG + threadIdx.x;
+    const int k = blockIdx.y;
+    const int b = blockIdx.z;
+    const bool act = d < D;
+    const int dc = act ? d : D - 1;
+    float A2[NS];
+    load_A2(A_log, dc, A2);
+    const float bias = dt_bias ? dt_bias[dc] : 0.0f;
+    const float Dd = Dp ? Dp[dc] : 0.0f;
+    float h[NS];
+    if (k > 0) {
+        load_state(starts + (((int64_t)b * start_nent + (int64_t)k * start_kstep) * D + dc) * NS, h);
+    } else if (h0) {
+        load_state(h0 + ((int64_t)b * D + dc) * NS, h);
+    } else {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+    }
+    const int t0 = k * Tc, t1 = min(t0 + Tc, L);
+    const int64_t row0 = (int64_t)b * L + t0;
+    const T* xp = x + row0 * D + dc;
+    const T* dp = dt + row0 * D + dc;
+    const T* zp = GATE ? z + row0 * D + dc : nullptr;
+    const T* bp = Bm + row0 * NS;
+    const T* cp = Cm + row0 * NS;
+    T* yp = y + row0 * D + d;
+    for (int ts = t0; ts < t1; ts += TS) {
+        // checkpoint: state before token ts (chunk starts k>0 come from the carry kernel)
+        if (ckpt && act && (ts > t0 || k == 0))
+            store_state(ckpt + (((int64_t)b * nck + ts / TS) * D + d) * NS, h);
+        const int te = min(ts + TS, t1);
+        for (int t = ts; t < te; ++t, xp += D, dp += D, bp += NS, cp += NS, yp += D) {
+            const float xv = to_f(*xp), dtv = to_f(*dp);
+            const float zv = GATE ? to_f(*zp) : 0.0f;
+            if (GATE) zp += D;
+            float Bv[NS], Cv[NS];
+            load16(bp, Bv);
+            load16(cp, Cv);
+            float sg;
+            const float delta = softplus_sig(dtv + bias, sg);
+            const float acc = scan_token(h, A2, Bv, Cv, delta, xv);
+            const float yv = finish_y<GATE>(acc, Dd, xv, zv);
+            if (act) *yp = from_f<T>(yv);
+        }
+    }
+    if (h_last && act && k == K - 1) store_state(h_last + ((int64_t)b * D + d) * NS, h);
+}
+
+// ==================================================================== backward
+
+// (1) zero-end adjoint G of chunk k (k = 1..K-1) and its delta sum:
+//     walking the chunk backwards, lam <- (lam + C_t g_t) * exp(delta_t A).
+template <typename T, bool GATE>
+__global__ __launch_bounds__(WG) void k_bwd_chunk(
+    const T* __restrict__ dt, const T* __restrict__ Cm, const T* __restrict__ z,
+    const T* __restrict__ dy, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    float* __restrict__ wsG, float* __restrict__ wsSum, int L, int D, int Tc, int K) {
+    const int d = blockIdx.x * WG + threadIdx.x;
+    const int k = blockIdx.y + 1;
+    const int b = blockIdx.z;
+    const bool act = d < D;
+    const int dc = act ? d : D - 1;
+    float A2[NS];
+    load_A2(A_log, dc, A2);
+    const float bias = dt_bias ? dt_bias[dc] : 0.0f;
+    float lam[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) lam[n] = 0.0f;
+    float sumd = 0.0f;
+    const int t0 = k * Tc, t1 = min(t0 + Tc, L);
+    const int64_t rowl = (int64_t)b * L + (t1 - 1);
+    const T* dp = dt + rowl * D + dc;
+    const T* zp = GATE ? z + rowl * D + dc : nullptr;
+    const T* gp = dy + rowl * D + dc;
+    const T* cp = Cm + rowl * NS;
+    for (int t = t1 - 1; t >= t0; --t, dp -= D, gp -= D, cp -= NS) {
+        const float dtv = to_f(*dp), dyv = to_f(*gp);
+        float g = dyv;
+        if (GATE) {
+            const float zv = to_f(*zp);
+            zp -= D;
+            g = dyv * (zv * sigmoid_f(zv));
+        }
+        float Cv[NS];
+        load16(cp, Cv);
+        float sg;
+        const float delta = softplus_sig(dtv + bias, sg);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const float a = __builtin_amdgcn_exp2f(delta * A2[n]);
+            lam[n] = __builtin_fmaf(Cv[n], g, lam[n]) * a;
+        }
+        sumd += delta;
+    }
+    if (act) {
+        const int64_t e = ((int64_t)b * (K - 1) + (k - 1)) * D + d;
+        store_state(wsG + e * NS, lam);
+        wsSum[e] = sumd;
+    }
+}
+
+// (2) adjoint entering each chunk from the right: Xin(b, k) = dL/dh at the
+//     chunk's last token from all later tokens; walks chunks in reverse.
+__global__ __launch_bounds__(WG) void k_bwd_carry(
+    const float* __restrict__ A_log, const float* __restrict__ wsG,
+    const float* __restrict__ wsSum, float* __restrict__ Xin, int D, int K) {
+    const int d = blockIdx.x * WG + threadIdx.x;
+    const int b = blockIdx.z;
+    if (d >= D) return;
+    float A2[NS];
+    load_A2(A_log, d, A2);
+    float X[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) X[n] = 0.0f;
+    for (int k = K - 1; k >= 0; --k) {
+        store_state(Xin + (((int64_t)b * K + k) * D + d) * NS, X);
+        if (k == 0) break;
+        const int64_t e = ((int64_t)b * (K - 1) + (k - 1)) * D + d;
+        float G[NS];
+        load_state(wsG + e * NS, G);
+        const float sumd = wsSum[e];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const float P = __builtin_amdgcn_exp2f(A2[n] * sumd);
+            X[n] = __builtin_fmaf(P, X[n], G[n]);
+        }
+    }
+}
+
+// Sum of 32 per-lane values over the 64 lanes of a wave through LDS; lanes
+// 0..31 return the sums (value index = lane), others return garbage.
+__device__ __forceinline__ float wave_sum32(const float dBp[NS], const float dCp[NS],
+                                            float* __restrict__ scr) {
+    constexpr int RS = 36;  // row stride (floats): 16-byte aligned rows, conflict-free column reads
+    const int lane = threadIdx.x & 63;
+    float4* row = reinterpret_cast<float4*>(scr + lane * RS);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) row[i] = make_float4(dBp[4 * i], dBp[4 * i + 1], dBp[4 * i + 2], dBp[4 * i + 3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) row[4 + i] = make_float4(dCp[4 * i], dCp[4 * i + 1], dCp[4 * i + 2], dCp[4 * i + 3]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int v = lane & 31, half = lane >> 5;
+    const float* col = scr + (half * 32) * RS + v;
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) s += col[r * RS];
+    s += __shfl_xor(s, 32);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return s;
+}
+
+// (3) per chunk: adjoint sweep in reverse over blocks of TS tokens.  Each block
+//     recomputes its TS+1 states from the checkpoint, then walks backwards:
+//       lam  += C_t g_t                       (g_t = dy_t silu(z_t))
+//       dx    = delta sum_n lam B + D g       dB[t,n] += lam delta x (channel sum)
+//       dC[t,n] += g h_t                       ddelta = sum_n lam (A a h_{t-1} + B x)
+//       dA[n] += lam a h_{t-1} delta           lam <- lam a
+template <typename T, bool GATE>
+__global__ __launch_bounds__(WG) void k_bwd_main(
+    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
+    const T* __restrict__ Cm, const T* __restrict__ z, const T* __restrict__ dy,
+    const float* __restrict__ A_log, const float* __restrict__ Dp,
+    const float* __restrict__ dt_bias, const float* __restrict__ ckpt,
+    const float* __restrict__ Xin, T* __restrict__ dxo, T* __restrict__ ddto,
+    T* __restrict__ dzo, float* __restrict__ dh0, float* __restrict__ wsBC,
+    float* __restrict__ wsPA, float* __restrict__ wsPD, int L, int D, int Tc, int K,
+    int64_t nck, int ndb) {
+    __shared__ float scr[NWAVE][64 * 36];
+    __shared__ float wres[NWAVE][TS][32];
+    const int d = blockIdx.x * WG + threadIdx.x;
+    const int k = blockIdx.y;
+    const int b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool act = d < D;
+    const int dc = act ? d : D - 1;
+    float A2[NS];
+    load_A2(A_log, dc, A2);
+    const float bias = dt_bias ? dt_bias[dc] : 0.0f;
+    const float Dd = Dp ? Dp[dc] : 0.0f;
+    float lam[NS], dA[NS];
+    if (Xin && act) load_state(Xin + (((int64_t)b * K + k) * D + d) * NS, lam);
+    else {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) lam[n] = 0.0f;
+    }
+#pragma unroll
+    for (int n = 0; n < NS; ++n) dA[n] = 0.0f;
+    float dDacc = 0.0f, ddtbacc = 0.0f;
+    const int t0 = k * Tc, t1 = min(t0 + Tc, L);
+    const int j0 = t0 / TS, j1 = (t1 + TS - 1) / TS;
+    for (int j = j1 - 1; j >= j0; --j) {
+        const int ts = j * TS;
+        const int cnt = min(TS, t1 - ts);
+        const int64_t row0 = (int64_t)b * L + ts;
+        float hc[TS + 1][NS];
+        load_state(ckpt + (((int64_t)b * nck + j) * D + dc) * NS, hc[0]);
+        // recompute the block's states
+#pragma unroll
+        for (int i = 0; i < TS; ++i) {
+            if (i < cnt) {
+                const int64_t row = row0 + i;
+                const float xv = to_f(x[row * D + dc]), dtv = to_f(dt[row * D + dc]);
+                float Bv[NS];
+                load16(Bm + row * NS, Bv);
+                float sg;
+                const float delta = softplus_sig(dtv + bias, sg);
+                const float dxv = delta * xv;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    const float a = __builtin_amdgcn_exp2f(delta * A2[n]);
+                    hc[i + 1][n] = __builtin_fmaf(a, hc[i][n], dxv * Bv[n]);
+                }
+            }
+        }
+        // reverse sweep
+#pragma unroll
+        for (int i = TS - 1; i >= 0; --i) {
+            if (i < cnt) {
+                const int64_t row = row0 + i;
+                const float xv = to_f(x[row * D + dc]), dtv = to_f(dt[row * D + dc]);
+                const float dyv = to_f(dy[row * D + dc]);
+                float Bv[NS], Cv[NS];
+                load16(Bm + row * NS, Bv);
+                load16(Cm + row * NS, Cv);
+                float sg;
+                const float delta = softplus_sig(dtv + bias, sg);
+                const float dxv = delta * xv;
+                float zv = 0.0f, sz = 0.0f, g = dyv;
+                if (GATE) {
+                    zv = to_f(z[row * D + dc]);
+                    sz = sigmoid_f(zv);
+                    g = dyv * (zv * sz);
+                }
+                if (!act) g = 0.0f;
+                float s1 = 0.0f, s2 = 0.0f, yacc = 0.0f;
+                float dBp[NS], dCp[NS];
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    const float a = __builtin_amdgcn_exp2f(delta * A2[n]);
+                    if (GATE) yacc = __builtin_fmaf(Cv[n], hc[i + 1][n], yacc);
+                    lam[n] = __builtin_fmaf(Cv[n], g, lam[n]);
+                    s1 = __builtin_fmaf(lam[n], Bv[n], s1);
+                    dBp[n] = lam[n] * dxv;
+                    dCp[n] = g * hc[i + 1][n];
+                    const float lp = lam[n] * a;
+                    const float gg = lp * hc[i][n];
+                    s2 = __builtin_fmaf(A2[n], gg, s2);
+                    dA[n] = __builtin_fmaf(delta, gg, dA[n]);
+                    lam[n] = lp;
+                }
+                s2 *= LN2;  // A = A2 * ln 2
+                const float dxv_out = __builtin_fmaf(delta, s1, Dd * g);
+                const float ddelta = __builtin_fmaf(xv, s1, s2);
+                const float ddtv = ddelta * sg;
+                if (act) {
+                    dxo[row * D + d] = from_f<T>(dxv_out);
+                    ddto[row * D + d] = from_f<T>(ddtv);
+                    if (GATE) {
+                        const float ypre = __builtin_fmaf(Dd, xv, yacc);
+                        const float dzv = dyv * ypre * sz * (1.0f + zv * (1.0f - sz));
+                        dzo[row * D + d] = from_f<T>(dzv);
+                    }
+                    dDacc = __builtin_fmaf(g, xv, dDacc);
+                    ddtbacc += ddtv;
+                }
+                const float s = wave_sum32(dBp, dCp, scr[wave]);
+                if (lane < 32) wres[wave][i][lane] = s;
+            }
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < cnt * 32; idx += WG) {
+            const int i = idx >> 5, v = idx & 31;
+            float s = wres[0][i][v];
+#pragma unroll
+            for (int w = 1; w < NWAVE; ++w) s += wres[w][i][v];
+            wsBC[((row0 + i) * ndb + blockIdx.x) * 32 + v] = s;
+        }
+        __syncthreads();
+    }
+    if (act) {
+        const int64_t e = ((int64_t)b * K + k) * D + d;
+        store_state(wsPA + e * NS, dA);
+        wsPD[e * 2 + 0] = dDacc;
+        wsPD[e * 2 + 1] = ddtbacc;
+        if (dh0 && k == 0) store_state(dh0 + ((int64_t)b * D + d) * NS, lam);
+    }
+}
+
+// dB/dC: fixed-order sum over channel blocks.  One thread per (b, t, value).
+template <typename T>
+__global__ __launch_bounds__(WG) void k_bwd_reduce_bc(const float* __restrict__ wsBC,
+                                                      T* __restrict__ dB, T* __restrict__ dC,
+                                                      int64_t rows, int ndb) {
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (i >= rows * 32) return;
+    const int64_t row = i >> 5;
+    const int v = (int)(i & 31);
+    const float* p = wsBC + row * ndb * 32 + v;
+    float s = 0.0f;
+    for (int blk = 0; blk < ndb; ++blk) s += p[blk * 32];
+    if (v < NS) dB[row * NS + v] = from_f<T>(s);
+    else dC[row * NS + (v - NS)] = from_f<T>(s);
+}
+
+// dA_log = A * sum dA, dD, ddt_bias: fixed-order sums over (batch, chunk).
+__global__ __launch_bounds__(WG) void k_bwd_reduce_params(
+    const float* __restrict__ A_log, const float* __restrict__ wsPA,
+    const float* __restrict__ wsPD, float* __restrict__ dA_log, float* __restrict__ dDo,
+    float* __restrict__ ddt_bias, int Bt, int K, int D) {
+    const int i = blockIdx.x * WG + threadIdx.x;
+    if (i < D * NS) {
+        const int d = i / NS, n = i % NS;
+        float s = 0.0f;
+        for (int b = 0; b < Bt; ++b)
+            for (int k = 0; k < K; ++k) s += wsPA[(((int64_t)b * K + k) * D + d) * NS + n];
+        dA_log[i] = s * -expf(A_log[i]);
+    } else if (i < D * NS + D) {
+        const int d = i - D * NS;
+        float s0 = 0.0f, s1 = 0.0f;
+        for (int b = 0; b < Bt; ++b)
+            for (int k = 0; k < K; ++k) {
+                const int64_t e = ((int64_t)b * K + k) * D + d;
+                s0 += wsPD[e * 2 + 0];
+                s1 += wsPD[e * 2 + 1];
+            }
+        if (dDo) dDo[d] = s0;
+        ddt_bias[d] = s1;
+    }
+}
+
+// ======================================================================= step
+template <typename T, bool GATE>
+__global__ __launch_bounds__(WG) void k_step(
+    float* __restrict__ h, const T* __restrict__ x, const T* __restrict__ dt,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const T* __restrict__ z,
+    const float* __restrict__ A_log, const float* __restrict__ Dp,
+    const float* __restrict__ dt_bias, T* __restrict__ y, int D) {
+    const int d = blockIdx.x * WG + threadIdx.x;
+    const int b = blockIdx.z;
+    if (d >= D) return;
+    float A2[NS];
+    load_A2(A_log, d, A2);
+    const float bias = dt_bias ? dt_bias[d] : 0.0f;
+    const float Dd = Dp ? Dp[d] : 0.0f;
+    const int64_t i = (int64_t)b * D + d;
+    float hs[NS];
+    load_state(h + i * NS, hs);
+    float Bv[NS], Cv[NS];
+    load16(Bm + (int64_t)b * NS, Bv);
+    load16(Cm + (int64_t)b * NS, Cv);
+    const float xv = to_f(x[i]), dtv = to_f(dt[i]);
+    const float zv = GATE ? to_f(z[i]) : 0.0f;
+    float sg;
+    const float delta = softplus_sig(dtv + bias, sg);
+    const float acc = scan_token(hs, A2, Bv, Cv, delta, xv);
+    y[i] = from_f<T>(finish_y<GATE>(acc, Dd, xv, zv));
+    store_state(h + i * NS, hs);
+}
+
+// Fills used when seqlen == 0: dst[i] = src ? src[i] : 0.
+__global__ __launch_bounds__(WG) void k_fill(float* __restrict__ dst, const float* __restrict__ src,
+                                             int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+// ================================================================ host side
+
+struct Plan {
+    int64_t Bt, L, D;
+    int io;
+    int64_t Tc, K, nck, ndb;
+};
+
+ssm_status check_dims(const ssm_dims* d) {
+    if (!d) return SSM_E_NULLPTR;
+    if (d->batch < 1 || d->seqlen < 0 || d->d_inner < 1 || d->d_state < 1) return SSM_E_SHAPE;
+    if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_E_DTYPE;
+    if (d->d_state != NS) return SSM_E_UNSUPPORTED;
+    if (d->batch > 65535) return SSM_E_UNSUPPORTED;
+    // kernels index tokens and channels with 32-bit ints
+    if (d->seqlen > (int64_t)1 << 30 || d->d_inner > (int64_t)1 << 30) return SSM_E_UNSUPPORTED;
+    return SSM_OK;
+}
+
+Plan make_plan(const ssm_dims* d) {
+    Plan p;
+    p.Bt = d->batch;
+    p.L = d->seqlen;
+    p.D = d->d_inner;
+    p.io = d->io_dtype;
+    const int64_t lanes = p.Bt * p.D;
+    int64_t kt = (TARGET_LANES + lanes - 1) / lanes;
+    kt = std::min<int64_t>(kt, p.L / MIN_CHUNK);
+    kt = std::min<int64_t>(kt, 4096);  // grid.y limit with margin
+    if (kt < 1) kt = 1;
+    int64_t tc = (p.L + kt - 1) / kt;
+    tc = (tc + TS - 1) / TS * TS;
+    if (tc < TS) tc = TS;
+    p.Tc = tc;
+    p.K = p.L > 0 ? (p.L + tc - 1) / tc : 1;
+    p.nck = (p.L + TS - 1) / TS;
+    p.ndb = (p.D + WG - 1) / WG;
+    return p;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct FwdWs {
+    size_t S, sum, starts, total;
+};
+FwdWs fwd_ws(const Plan& p) {
+    FwdWs w{0, 0, 0, 0};
+    if (p.K > 1) {
+        w.S = 0;
+        w.sum = w.S + align_up(sizeof(float) * p.Bt * (p.K - 1) * p.D * NS);
+        w.starts = w.sum + align_up(sizeof(float) * p.Bt * (p.K - 1) * p.D);
+        w.total = w.starts + align_up(sizeof(float) * p.Bt * p.K * p.D * NS);
+    }
+    return w;
+}
+
+struct BwdWs {
+    size_t G, sum, X, BC, PA, PD, total;
+};
+BwdWs bwd_ws(const Plan& p) {
+    BwdWs w{};
+    size_t off = 0;
+    if (p.K > 1) {
+        w.G = off; off += align_up(sizeof(float) * p.Bt * (p.K - 1) * p.D * NS);
+        w.sum = off; off += align_up(sizeof(float) * p.Bt * (p.K - 1) * p.D);
+        w.X = off; off += align_up(sizeof(float) * p.Bt * p.K * p.D * NS);
+    }
+    w.BC = off; off += align_up(sizeof(float) * p.Bt * p.L * p.ndb * 32);
+    w.PA = off; off += align_up(sizeof(float) * p.Bt * p.K * p.D * NS);
+    w.PD = off; off += align_up(sizeof(float) * p.Bt * p.K * p.D * 2);
+    w.total = off;
+    return w;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+struct Launcher {
+    hipStream_t s;
+    ssm_timing* tm;
+    template <typename... KArgs, typename... Args>
+    ssm_status operator()(int kid, void (*kern)(KArgs...), dim3 grid, Args... args) {
+        const bool rec = tm && tm->events && tm->count < tm->capacity && tm->count < SSM_TIMING_MAX;
+        if (rec) (void)hipEventRecord(tm->events[2 * tm->count], s);
+        hipLaunchKernelGGL(kern, grid, dim3(WG), 0, s, args...);
+        const hipError_t e = hipGetLastError();
+        if (rec) {
+            (void)hipEventRecord(tm->events[2 * tm->count + 1], s);
+            tm->kernel_id[tm->count] = kid;
+            tm->count++;
+        }
+        return e == hipSuccess ? SSM_OK : SSM_E_LAUNCH;
+    }
+};
+
+#define SSM_TRY(expr)                       \
+    do {                                    \
+        const ssm_status st_ = (expr);      \
+        if (st_ != SSM_OK) return st_;      \
+    } while (0)
+
+template <typename T, bool GATE>
+ssm_status run_fwd(const Plan& p, const void* x, const void* dt, const void* B, const void* C,
+                   const void* z, const float* A_log, const float* Dp, const float* dt_bias,
+                   const float* h0, void* y, float* h_last, float* ckpt, void* ws,
+                   Launcher& launch) {
+    const FwdWs w = fwd_ws(p);
+    char* wsb = static_cast<char*>(ws);
+    float* S = p.K > 1 ? reinterpret_cast<float*>(wsb + w.S) : nullptr;
+    float* sum = p.K > 1 ? reinterpret_cast<float*>(wsb + w.sum) : nullptr;
+    float* starts;
+    int64_t nent, kstep;
+    if (ckpt) {
+        starts = ckpt;
+        nent = p.nck;
+        kstep = p.Tc / TS;
+    } else {
+        starts = p.K > 1 ? reinterpret_cast<float*>(wsb + w.starts) : nullptr;
+        nent = p.K;
+        kstep = 1;
+    }
+    const int L = (int)p.L, D = (int)p.D, Tc = (int)p.Tc, K = (int)p.K;
+    if (p.K > 1) {
+        SSM_TRY(launch(SSM_K_FWD_CHUNK, k_fwd_chunk<T>, dim3(p.ndb, p.K - 1, p.Bt),
+                       (const T*)x, (const T*)dt, (const T*)B, A_log, dt_bias, S, sum, L, D, Tc, K));
+        SSM_TRY(launch(SSM_K_FWD_CARRY, k_fwd_carry, dim3(p.ndb, 1, p.Bt), A_log, h0,
+                       (const float*)S, (const float*)sum, starts, D, K, nent, kstep));
+    }
+    return launch(SSM_K_FWD_MAIN, k_fwd_main<T, GATE>, dim3(p.ndb, p.K, p.Bt), (const T*)x,
+                  (const T*)dt, (const T*)B, (const T*)C, (const T*)z, A_log, Dp, dt_bias, h0,
+                  (const float*)starts, (T*)y, h_last, ckpt, L, D, Tc, K, (int64_t)p.nck, nent,
+                  kstep);
+}
+
+template <typename T, bool GATE>
+ssm_status run_bwd(const Plan& p, const void* x, const void* dt, const void* B, const void* C,
+                   const void* z, const float* A_log, const float* Dp, const float* dt_bias,
+                   const float* ckpt, const void* dy, void* dx, void* ddt, void* dB, void* dC,
+                   void* dz, float* dA_log, float* dD, float* ddt_bias, float* dh0, void* ws,
+                   Launcher& launch) {
+    const BwdWs w = bwd_ws(p);
+    char* wsb = static_cast<char*>(ws);
+    float* G = p.K > 1 ? reinterpret_cast<float*>(wsb + w.G) : nullptr;
+    float* sum = p.K > 1 ? reinterpret_cast<float*>(wsb + w.sum) : nullptr;
+    float* X = p.K > 1 ? reinterpret_cast<float*>(wsb + w.X) : nullptr;
+    float* BC = reinterpret_cast<float*>(wsb + w.BC);
+    float* PA = reinterpret_cast<float*>(wsb + w.PA);
+    float* PD = reinterpret_cast<float*>(wsb + w.PD);
+    const int L = (int)p.L, D = (int)p.D, Tc = (int)p.Tc, K = (int)p.K;
+    if (p.K > 1) {
+        SSM_TRY(launch(SSM_K_BWD_CHUNK, k_bwd_chunk<T, GATE>, dim3(p.ndb, p.K - 1, p.Bt),
+                       (const T*)dt, (const T*)C, (const T*)z, (const T*)dy, A_log, dt_bias, G,
+                       sum, L, D, Tc, K));
+        SSM_TRY(launch(SSM_K_BWD_CARRY, k_bwd_carry, dim3(p.ndb, 1, p.Bt), A_log,
+                       (const float*)G, (const float*)sum, X, D, K));
+    }
+    SSM_TRY(launch(SSM_K_BWD_MAIN, k_bwd_main<T, GATE>, dim3(p.ndb, p.K, p.Bt), (const T*)x,
+                   (const T*)dt, (const T*)B, (const T*)C, (const T*)z, (const T*)dy, A_log, Dp,
+                   dt_bias, ckpt, (const float*)X, (T*)dx, (T*)ddt, (T*)dz, dh0, BC, PA, PD, L,
+                   D, Tc, K, (int64_t)p.nck, (int)p.ndb));
+    const int64_t rows = p.Bt * p.L;
+    SSM_TRY(launch(SSM_K_BWD_REDUCE_BC, k_bwd_reduce_bc<T>, dim3((unsigned)((rows * 32 + WG - 1) / WG)),
+                   (const float*)BC, (T*)dB, (T*)dC, rows, (int)p.ndb));
+    const int64_t np = p.D * NS + p.D;
+    return launch(SSM_K_BWD_REDUCE_P, k_bwd_reduce_params, dim3((unsigned)((np + WG - 1) / WG)),
+                  A_log, (const float*)PA, (const float*)PD, dA_log, dD, ddt_bias, (int)p.Bt,
+                  (int)p.K, D);
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+extern "C" {
+
+const char* ssm_status_str(ssm_status s) {
+    switch (s) {
+        case SSM_OK: return "ok";
+        case SSM_E_NULLPTR: return "required pointer is NULL";
+        case SSM_E_SHAPE: return "dimension out of range";
+        case SSM_E_DTYPE: return "unknown io dtype";
+        case SSM_E_ALIGN: return "pointer not 16-byte aligned";
+        case SSM_E_WORKSPACE: return "workspace too small";
+        case SSM_E_LAUNCH: return "kernel launch failed";
+        case SSM_E_UNSUPPORTED: return "unsupported configuration (d_state must be 16, batch <= 65535)";
+    }
+    return "unknown status";
+}
+
+const char* ssm_kernel_name(int32_t id) {
+    switch (id) {
+        case SSM_K_FWD_CHUNK: return "k_fwd_chunk";
+        case SSM_K_FWD_CARRY: return "k_fwd_carry";
+        case SSM_K_FWD_MAIN: return "k_fwd_main";
+        case SSM_K_BWD_CHUNK: return "k_bwd_chunk";
+        case SSM_K_BWD_CARRY: return "k_bwd_carry";
+        case SSM_K_BWD_MAIN: return "k_bwd_main";
+        case SSM_K_BWD_REDUCE_BC: return "k_bwd_reduce_bc";
+        case SSM_K_BWD_REDUCE_P: return "k_bwd_reduce_params";
+        case SSM_K_STEP: return "k_step";
+        case SSM_K_FILL: return "k_fill";
+    }
+    return "?";
+}
+
+size_t ssm_scan_ckpt_bytes(const ssm_dims* dims) {
+    if (check_dims(dims) != SSM_OK) return 0;
+    const Plan p = make_plan(dims);
+    return sizeof(float) * (size_t)(p.Bt * p.nck * p.D * NS);
+}
+
+size_t ssm_scan_fwd_workspace_bytes(const ssm_dims* dims) {
+    if (check_dims(dims) != SSM_OK) return 0;
+    return fwd_ws(make_plan(dims)).total;
+}
+
+size_t ssm_scan_bwd_workspace_bytes(const ssm_dims* dims) {
+    if (check_dims(dims) != SSM_OK) return 0;
+    const Plan p = make_plan(dims);
+    if (p.L == 0) return 0;
+    return bwd_ws(p).total;
+}
+
+ssm_status ssm_scan_fwd(const ssm_dims* dims, const void* x, const void* dt, const void* B,
+                        const void* C, const void* z, const float* A_log, const float* D,
+                        const float* dt_bias, const float* h0, void* y, float* h_last,
+                        float* ckpt, void* ws, size_t ws_bytes, hipStream_t stream,
+                        ssm_timing* timing) {
+    SSM_TRY(check_dims(dims));
+    const Plan p = make_plan(dims);
+    if (!A_log) return SSM_E_NULLPTR;
+    if (p.L > 0 && (!x || !dt || !B || !C || !y)) return SSM_E_NULLPTR;
+    const void* ptrs[] = {x, dt, B, C, z, A_log, D, dt_bias, h0, y, h_last, ckpt, ws};
+    for (const void* q : ptrs)
+        if (q && misaligned(q)) return SSM_E_ALIGN;
+    const size_t need = fwd_ws(p).total;
+    if (p.L > 0 && need > 0 && (!ws || ws_bytes < need)) return SSM_E_WORKSPACE;
+    (void)hipGetLastError();
+    Launcher launch{stream, timing};
+    if (p.L == 0) {
+        if (!h_last) return SSM_OK;
+        const int64_t n = p.Bt * p.D * NS;
+        return launch(SSM_K_FILL, k_fill, dim3((unsigned)((n + WG - 1) / WG)), h_last, h0, n);
+    }
+    const bool gate = z != nullptr;
+    if (p.io == SSM_F32) {
+        return gate ? run_fwd<float, true>(p, x, dt, B, C, z, A_log, D, dt_bias, h0, y, h_last, ckpt, ws, launch)
+                    : run_fwd<float, false>(p, x, dt, B, C, z, A_log, D, dt_bias, h0, y, h_last, ckpt, ws, launch);
+    }
+    return gate ? run_fwd<bf16_t, true>(p, x, dt, B, C, z, A_log, D, dt_bias, h0, y, h_last, ckpt, ws, launch)
+                : run_fwd<bf16_t, false>(p, x, dt, B, C, z, A_log, D, dt_bias, h0, y, h_last, ckpt, ws, launch);
+}
+
+ssm_status ssm_scan_bwd(const ssm_dims* dims, const void* x, const void* dt, const void* B,
+                        const void* C, const void* z, const float* A_log, const float* D,
+                        const float* dt_bias, const float* h0, const float* ckpt,
+                        const void* dy, void* dx, void* ddt, void* dB, void* dC, void* dz,
+                        float* dA_log, float* dD, float* ddt_bias, float* dh0, void* ws,
+                        size_t ws_bytes, hipStream_t stream, ssm_timing* timing) {
+    (void)h0;  // the checkpoints already hold h0 (entry 0)
+    SSM_TRY(check_dims(dims));
+    const Plan p = make_plan(dims);
+    if (!A_log || !dA_log || !ddt_bias || (D && !dD)) return SSM_E_NULLPTR;
+    if (p.L > 0 && (!x || !dt || !B || !C || !ckpt || !dy || !dx || !ddt || !dB || !dC))
+        return SSM_E_NULLPTR;
+    if (p.L > 0 && z && !dz) return SSM_E_NULLPTR;
+    const void* ptrs[] = {x, dt, B, C, z, A_log, D, dt_bias, h0, ckpt, dy, dx, ddt, dB, dC, dz,
+                          dA_log, dD, ddt_bias, dh0, ws};
+    for (const void* q : ptrs)
+        if (q && misaligned(q)) return SSM_E_ALIGN;
+    const size_t need = p.L > 0 ? bwd_ws(p).total : 0;
+    if (need > 0 && (!ws || ws_bytes < need)) return SSM_E_WORKSPACE;
+    (void)hipGetLastError();
+    Launcher launch{stream, timing};
+    if (p.L == 0) {
+        const int64_t np = p.D * NS;
+        SSM_TRY(launch(SSM_K_FILL, k_fill, dim3((unsigned)((np + WG - 1) / WG)), dA_log,
+                       (const float*)nullptr, np));
+        SSM_TRY(launch(SSM_K_FILL, k_fill, dim3((unsigned)((p.D + WG - 1) / WG)), ddt_bias,
+                       (const float*)nullptr, p.D));
+        if (dD)
+            SSM_TRY(launch(SSM_K_FILL, k_fill, dim3((unsigned)((p.D + WG - 1) / WG)), dD,
+                           (const float*)nullptr, p.D));
+        if (dh0) {
+            const int64_t n = p.Bt * p.D * NS;
+            SSM_TRY(launch(SSM_K_FILL, k_fill, dim3((unsigned)((n + WG - 1) / WG)), dh0,
+                           (const float*)nullptr, n));
+        }
+        return SSM_OK;
+    }
+    const bool gate = z != nullptr;
+    if (p.io == SSM_F32) {
+        return gate ? run_bwd<float, true>(p, x, dt, B, C, z, A_log, D, dt_bias, ckpt, dy, dx, ddt, dB, dC, dz, dA_log, dD, ddt_bias, dh0, ws, launch)
+                    : run_bwd<float, false>(p, x, dt, B, C, z, A_log, D, dt_bias, ckpt, dy, dx, ddt, dB, dC, dz, dA_log, dD, ddt_bias, dh0, ws, launch);
+    }
+    return gate ? run_bwd<bf16_t, true>(p, x, dt, B, C, z, A_log, D, dt_bias, ckpt, dy, dx, ddt, dB, dC, dz, dA_log, dD, ddt_bias, dh0, ws, launch)
+                : run_bwd<bf16_t, false>(p, x, dt, B, C, z, A_log, D, dt_bias, ckpt, dy, dx, ddt, dB, dC, dz, dA_log, dD, ddt_bias, dh0, ws, launch);
+}
+
+ssm_status ssm_scan_step(int64_t batch, int64_t d_inner, int64_t d_state, int32_t io_dtype,
+                         float* h, const void* x, const void* dt, const void* B, const void* C,
+                         const void* z, const float* A_log, const float* D,
+                         const float* dt_bias, void* y, hipStream_t stream, ssm_timing* timing) {
+    ssm_dims dims{batch, 1, d_inner, d_state, io_dtype};
+    SSM_TRY(check_dims(&dims));
+    if (!h || !x || !dt || !B || !C || !A_log || !y) return SSM_E_NULLPTR;
+    const void* ptrs[] = {h, x, dt, B, C, z, A_log, D, dt_bias, y};
+    for (const void* q : ptrs)
+        if (q && misaligned(q)) return SSM_E_ALIGN;
+    (void)hipGetLastError();
+    Launcher launch{stream, timing};
+    const dim3 grid((unsigned)((d_inner + WG - 1) / WG), 1, (unsigned)batch);
+    const int Dn = (int)d_inner;
+    if (io_dtype == SSM_F32) {
+        return z ? launch(SSM_K_STEP, k_step<float, true>, grid, h, (const float*)x, (const float*)dt, (const float*)B, (const float*)C, (const float*)z, A_log, D, dt_bias, (float*)y, Dn)
+                 : launch(SSM_K_STEP, k_step<float, false>, grid, h, (const float*)x, (const float*)dt, (const float*)B, (const float*)C, (const float*)z, A_log, D, dt_bias, (float*)y, Dn);
+    }
+    return z ? launch(SSM_K_STEP, k_step<bf16_t, true>, grid, h, (const bf16_t*)x, (const bf16_t*)dt, (const bf16_t*)B, (const bf16_t*)C, (const bf16_t*)z, A_log, D, dt_bias, (bf16_t*)y, Dn)
+             : launch(SSM_K_STEP, k_step<bf16_t, false>, grid, h, (const bf16_t*)x, (const bf16_t*)dt, (const bf16_t*)B, (const bf16_t*)C, (const bf16_t*)z, A_log, D, dt_bias, (bf16_t*)y, Dn);
+}
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched):
+the library loads, exports every function include/ssm_scan.h declares, and
+rejects bad arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+ssm = pytest.importorskip("selective_state_space_04_amd")
+lib = ssm.library()
+
+OK, NULLPTR, SHAPE, DTYPE, ALIGN, WORKSPACE, LAUNCH, UNSUPPORTED = range(8)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_exports_present():
+    names = _declared_functions()
+    assert {"ssm_scan_fwd", "ssm_scan_bwd", "ssm_scan_step", "ssm_scan_ckpt_bytes",
+            "ssm_scan_fwd_workspace_bytes", "ssm_scan_bwd_workspace_bytes", "ssm_status_str",
+            "ssm_kernel_name"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ssm_scan.h but not exported"
+
+
+def test_status_strings():
+    for code in range(8):
+        assert ssm.status_str(code)
+    assert ssm.status_str(99) == "unknown status"
+
+
+def _dims(b=2, L=64, d=32, n=16, io=0):
+    return ssm.SsmDims(b, L, d, n, io)
+
+
+def test_query_sizes():
+    d = _dims(2, 64, 32)
+    assert lib.ssm_scan_ckpt_bytes(ctypes.byref(d)) == 4 * 2 * 8 * 32 * 16  # state every 8 tokens
+    assert lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(d)) == 0          # one chunk: no carries
+    assert lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d)) > 0
+    for bad in (_dims(0), _dims(L=-1), _dims(d=0), _dims(n=8), _dims(io=5)):
+        assert lib.ssm_scan_ckpt_bytes(ctypes.byref(bad)) == 0
+        assert lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(bad)) == 0
+    big = _dims(8, 2048, 1536)
+    assert lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(big)) > 0       # chunked sequence
+
+
+FAKE = 1 << 20  # 16-byte aligned non-null fake device address: never dereferenced
+
+
+def _fwd(dims, **over):
+    a = dict(x=FAKE, dt=FAKE, B=FAKE, C=FAKE, z=None, A_log=FAKE, D=None, dt_bias=None, h0=None,
+             y=FAKE, h_last=None, ckpt=None, ws=None, ws_bytes=0)
+    a.update(over)
+    P = ctypes.c_void_p
+    return lib.ssm_scan_fwd(ctypes.byref(dims) if dims is not None else None,
+                            *[P(a[k]) if a[k] else None for k in
+                              ("x", "dt", "B", "C", "z", "A_log", "D", "dt_bias", "h0", "y", "h_last", "ckpt", "ws")],
+                            a["ws_bytes"], None, None)
+
+
+def test_fwd_rejects_bad_arguments():
+    assert _fwd(None) == NULLPTR
+    assert _fwd(_dims(0)) == SHAPE
+    assert _fwd(_dims(d=0)) == SHAPE
+    assert _fwd(_dims(n=8)) == UNSUPPORTED
+    assert _fwd(_dims(b=70000)) == UNSUPPORTED
+    assert _fwd(_dims(io=2)) == DTYPE
+    assert _fwd(_dims(), x=None) == NULLPTR
+    assert _fwd(_dims(), A_log=None) == NULLPTR
+    assert _fwd(_dims(), y=None) == NULLPTR
+    assert _fwd(_dims(), dt=FAKE + 4) == ALIGN
+    assert _fwd(_dims(), z=FAKE + 2) == ALIGN
+    big = _dims(8, 2048, 1536)
+    need = lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(big))
+    assert _fwd(big) == WORKSPACE
+    assert _fwd(big, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+
+
+def _bwd(dims, **over):
+    a = dict(x=FAKE, dt=FAKE, B=FAKE, C=FAKE, z=None, A_log=FAKE, D=None, dt_bias=None, h0=None,
+             ckpt=FAKE, dy=FAKE, dx=FAKE, ddt=FAKE, dB=FAKE, dC=FAKE, dz=None, dA_log=FAKE, dD=None,
+             ddt_bias=FAKE, dh0=None, ws=None, ws_bytes=0)
+    a.update(over)
+    P = ctypes.c_void_p
+    keys = ("x", "dt", "B", "C", "z", "A_log", "D", "dt_bias", "h0", "ckpt", "dy", "dx", "ddt", "dB",
+            "dC", "dz", "dA_log", "dD", "ddt_bias", "dh0", "ws")
+    return lib.ssm_scan_bwd(ctypes.byref(dims), *[P(a[k]) if a[k] else None for k in keys],
+                            a["ws_bytes"], None, None)
+
+
+def test_bwd_rejects_bad_arguments():
+    d = _dims()
+    assert _bwd(_dims(n=32)) == UNSUPPORTED
+    assert _bwd(d, ckpt=None) == NULLPTR
+    assert _bwd(d, dy=None) == NULLPTR
+    assert _bwd(d, z=FAKE) == NULLPTR            # gate given but no dz output
+    assert _bwd(d, D=FAKE) == NULLPTR            # D given but no dD output
+    assert _bwd(d, dA_log=None) == NULLPTR
+    assert _bwd(d, dB=FAKE + 8) == ALIGN
+    need = lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert _bwd(d) == WORKSPACE
+    assert _bwd(d, ws=FAKE, ws_bytes=need - 256) == WORKSPACE
+
+
+def test_step_rejects_bad_arguments():
+    P = ctypes.c_void_p
+
+    def step(b=4, d=32, n=16, io=0, **over):
+        a = dict(h=FAKE, x=FAKE, dt=FAKE, B=FAKE, C=FAKE, z=None, A_log=FAKE, D=None, dt_bias=None, y=FAKE)
+        a.update(over)
+        keys = ("h", "x", "dt", "B", "C", "z", "A_log", "D", "dt_bias", "y")
+        return lib.ssm_scan_step(b, d, n, io, *[P(a[k]) if a[k] else None for k in keys], None, None)
+
+    assert step(b=0) == SHAPE
+    assert step(n=4) == UNSUPPORTED
+    assert step(io=7) == DTYPE
+    assert step(h=None) == NULLPTR
+    assert step(y=None) == NULLPTR
+    assert step(x=FAKE + 1) == ALIGN
+
+
+def test_binding_rejects_strided_and_mistyped_tensors():
+    import torch
+    x = torch.zeros(2, 8, 4).transpose(0, 1)
+    with pytest.raises((ValueError, TypeError)):
+        ssm.ssm_scan_fwd(x, x, torch.zeros(8, 2, 16), torch.zeros(8, 2, 16), None,
+                         torch.zeros(4, 16), None, None)
+    x = torch.zeros(2, 8, 4, dtype=torch.float64)
+    b = torch.zeros(2, 8, 16, dtype=torch.float64)
+    with pytest.raises(TypeError):
+        ssm.ssm_scan_fwd(x, x, b, b, None, torch.zeros(4, 16), None, None)

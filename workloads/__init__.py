@@ -43,12 +43,14 @@ CONFIGS = {
 def round_bf16(a):
     """Round an f32 array to the nearest-even bf16 value, returned as f32."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    out = u.astype(np.uint32).view(np.float32)
     nan = np.isnan(a)
+    u = a.view(np.uint32).copy()
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)           # no overflow for finite values
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    out = u.view(np.float32)
     if nan.any():
-        out = out.copy()
         out[nan] = np.nan
     return out
 
