@@ -106,18 +106,27 @@ __device__ __forceinline__ void load_A2(const float* __restrict__ A_log, int d, 
     for (int n = 0; n < NS; ++n) A2[n] = -expf(A_log[(int64_t)d * NS + n]) * LOG2E;
 }
 
-// Stable softplus(u) = max(u,0) + log1p(exp(-|u|)); also returns sigmoid(u),
-// its derivative.
+// Stable softplus(u) = max(u, 0) + log1p(e), e = exp(-|u|) in (0, 1], and
+// sigmoid(u) (its derivative).  log1p(e) comes from one hardware log2 through
+// the compensated form log1p(e) = log(w) * e / (w - 1), w = fl(1 + e): the
+// rounding of w cancels in the ratio, so the result stays within a few ulp
+// even when e is tiny (Goldberg, "What every computer scientist should know
+// about floating-point arithmetic", 1991, Theorem 4).
 __device__ __forceinline__ float softplus_sig(float u, float& sig) {
-    float e = __expf(-fabsf(u));
-    float r = __builtin_amdgcn_rcpf(1.0f + e);
+    const float e = __builtin_amdgcn_exp2f(-fabsf(u) * LOG2E);
+    const float w = 1.0f + e;
+    const float wm1 = w - 1.0f;
+    const float r = __builtin_amdgcn_rcpf(w);
     sig = u >= 0.0f ? r : e * r;
-    return fmaxf(u, 0.0f) + log1pf(e);
+    const float lp = wm1 == 0.0f
+                         ? e
+                         : (__builtin_amdgcn_logf(w) * LN2) * (e * __builtin_amdgcn_rcpf(wm1));
+    return fmaxf(u, 0.0f) + lp;
 }
 
 __device__ __forceinline__ float sigmoid_f(float z) {
-    float e = __expf(-fabsf(z));
-    float r = __builtin_amdgcn_rcpf(1.0f + e);
+    const float e = __builtin_amdgcn_exp2f(-fabsf(z) * LOG2E);
+    const float r = __builtin_amdgcn_rcpf(1.0f + e);
     return z >= 0.0f ? r : e * r;
 }
 
@@ -143,6 +152,15 @@ __device__ __forceinline__ float finish_y(float acc, float Dd, float xv, float z
     return ypre * (zv * sigmoid_f(zv));
 }
 
+// Streaming per-lane loads of one activation column (stride D elements); the
+// value of token i+1 is fetched while token i is processed.
+template <typename T>
+struct Stream {
+    const T* p;
+    int64_t stride;
+    __device__ __forceinline__ float at(int i) const { return to_f(p[(int64_t)i * stride]); }
+};
+
 // ===================================================================== forward
 
 // (1) zero-start end state S and delta sum of chunk k (k = 0 .. K-2).
@@ -163,15 +181,18 @@ __global__ __launch_bounds__(WG) void k_fwd_chunk(
 #pragma unroll
     for (int n = 0; n < NS; ++n) S[n] = 0.0f;
     float sumd = 0.0f;
-    const int t0 = k * Tc, t1 = min(t0 + Tc, L);
+    const int t0 = k * Tc, nt = min(Tc, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
-    const T* xp = x + row0 * D + dc;
-    const T* dp = dt + row0 * D + dc;
+    const Stream<T> xs{x + row0 * D + dc, D}, ds{dt + row0 * D + dc, D};
     const T* bp = Bm + row0 * NS;
-    for (int t = t0; t < t1; ++t, xp += D, dp += D, bp += NS) {
-        const float xv = to_f(*xp), dtv = to_f(*dp);
+    float xn = xs.at(0), dn = ds.at(0);
+    for (int i = 0; i < nt; ++i) {
+        const float xv = xn, dtv = dn;
+        const int ip = min(i + 1, nt - 1);
+        xn = xs.at(ip);
+        dn = ds.at(ip);
         float Bv[NS];
-        load16(bp, Bv);
+        load16(bp + (int64_t)i * NS, Bv);
         float sg;
         const float delta = softplus_sig(dtv + bias, sg);
         const float dxv = delta * xv;
@@ -247,32 +268,33 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
 #pragma unroll
         for (int n = 0; n < NS; ++n) h[n] = 0.0f;
     }
-    const int t0 = k * Tc, t1 = min(t0 + Tc, L);
+    const int t0 = k * Tc, nt = min(Tc, L - t0);
     const int64_t row0 = (int64_t)b * L + t0;
-    const T* xp = x + row0 * D + dc;
-    const T* dp = dt + row0 * D + dc;
-    const T* zp = GATE ? z + row0 * D + dc : nullptr;
+    const Stream<T> xs{x + row0 * D + dc, D}, ds{dt + row0 * D + dc, D};
+    const Stream<T> zs{GATE ? z + row0 * D + dc : nullptr, D};
     const T* bp = Bm + row0 * NS;
     const T* cp = Cm + row0 * NS;
     T* yp = y + row0 * D + d;
-    for (int ts = t0; ts < t1; ts += TS) {
-        // checkpoint: state before token ts (chunk starts k>0 come from the carry kernel)
-        if (ckpt && act && (ts > t0 || k == 0))
-            store_state(ckpt + (((int64_t)b * nck + ts / TS) * D + d) * NS, h);
-        const int te = min(ts + TS, t1);
-        for (int t = ts; t < te; ++t, xp += D, dp += D, bp += NS, cp += NS, yp += D) {
-            const float xv = to_f(*xp), dtv = to_f(*dp);
-            const float zv = GATE ? to_f(*zp) : 0.0f;
-            if (GATE) zp += D;
-            float Bv[NS], Cv[NS];
-            load16(bp, Bv);
-            load16(cp, Cv);
-            float sg;
-            const float delta = softplus_sig(dtv + bias, sg);
-            const float acc = scan_token(h, A2, Bv, Cv, delta, xv);
-            const float yv = finish_y<GATE>(acc, Dd, xv, zv);
-            if (act) *yp = from_f<T>(yv);
-        }
+    float* ck = ckpt ? ckpt + (((int64_t)b * nck + t0 / TS) * D + d) * NS : nullptr;
+    const int64_t ckstride = (int64_t)D * NS;
+    float xn = xs.at(0), dn = ds.at(0), zn = GATE ? zs.at(0) : 0.0f;
+    for (int i = 0; i < nt; ++i) {
+        // checkpoint: state before token t0+i (chunk starts k>0 come from the carry kernel)
+        if ((i & (TS - 1)) == 0 && ck && act && (i > 0 || k == 0))
+            store_state(ck + (int64_t)(i / TS) * ckstride, h);
+        const float xv = xn, dtv = dn, zv = zn;
+        const int ip = min(i + 1, nt - 1);
+        xn = xs.at(ip);
+        dn = ds.at(ip);
+        if (GATE) zn = zs.at(ip);
+        float Bv[NS], Cv[NS];
+        load16(bp + (int64_t)i * NS, Bv);
+        load16(cp + (int64_t)i * NS, Cv);
+        float sg;
+        const float delta = softplus_sig(dtv + bias, sg);
+        const float acc = scan_token(h, A2, Bv, Cv, delta, xv);
+        const float yv = finish_y<GATE>(acc, Dd, xv, zv);
+        if (act) yp[(int64_t)i * D] = from_f<T>(yv);
     }
     if (h_last && act && k == K - 1) store_state(h_last + ((int64_t)b * D + d) * NS, h);
 }
@@ -298,22 +320,21 @@ __global__ __launch_bounds__(WG) void k_bwd_chunk(
 #pragma unroll
     for (int n = 0; n < NS; ++n) lam[n] = 0.0f;
     float sumd = 0.0f;
-    const int t0 = k * Tc, t1 = min(t0 + Tc, L);
-    const int64_t rowl = (int64_t)b * L + (t1 - 1);
-    const T* dp = dt + rowl * D + dc;
-    const T* zp = GATE ? z + rowl * D + dc : nullptr;
-    const T* gp = dy + rowl * D + dc;
-    const T* cp = Cm + rowl * NS;
-    for (int t = t1 - 1; t >= t0; --t, dp -= D, gp -= D, cp -= NS) {
-        const float dtv = to_f(*dp), dyv = to_f(*gp);
-        float g = dyv;
-        if (GATE) {
-            const float zv = to_f(*zp);
-            zp -= D;
-            g = dyv * (zv * sigmoid_f(zv));
-        }
+    const int t0 = k * Tc, nt = min(Tc, L - t0);
+    const int64_t row0 = (int64_t)b * L + t0;
+    const Stream<T> ds{dt + row0 * D + dc, D}, gs{dy + row0 * D + dc, D};
+    const Stream<T> zs{GATE ? z + row0 * D + dc : nullptr, D};
+    const T* cp = Cm + row0 * NS;
+    float dn = ds.at(nt - 1), gn = gs.at(nt - 1), zn = GATE ? zs.at(nt - 1) : 0.0f;
+    for (int i = nt - 1; i >= 0; --i) {
+        const float dtv = dn, dyv = gn, zv = zn;
+        const int ip = max(i - 1, 0);
+        dn = ds.at(ip);
+        gn = gs.at(ip);
+        if (GATE) zn = zs.at(ip);
+        const float g = GATE ? dyv * (zv * sigmoid_f(zv)) : dyv;
         float Cv[NS];
-        load16(cp, Cv);
+        load16(cp + (int64_t)i * NS, Cv);
         float sg;
         const float delta = softplus_sig(dtv + bias, sg);
 #pragma unroll
@@ -358,38 +379,17 @@ __global__ __launch_bounds__(WG) void k_bwd_carry(
     }
 }
 
-// Sum of 32 per-lane values over the 64 lanes of a wave through LDS; lanes
-// 0..31 return the sums (value index = lane), others return garbage.
-__device__ __forceinline__ float wave_sum32(const float dBp[NS], const float dCp[NS],
-                                            float* __restrict__ scr) {
-    constexpr int RS = 36;  // row stride (floats): 16-byte aligned rows, conflict-free column reads
-    const int lane = threadIdx.x & 63;
-    float4* row = reinterpret_cast<float4*>(scr + lane * RS);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) row[i] = make_float4(dBp[4 * i], dBp[4 * i + 1], dBp[4 * i + 2], dBp[4 * i + 3]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) row[4 + i] = make_float4(dCp[4 * i], dCp[4 * i + 1], dCp[4 * i + 2], dCp[4 * i + 3]);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int v = lane & 31, half = lane >> 5;
-    const float* col = scr + (half * 32) * RS + v;
-    float s = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 32; ++r) s += col[r * RS];
-    s += __shfl_xor(s, 32);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    return s;
-}
-
 // (3) per chunk: adjoint sweep in reverse over blocks of TS tokens.  Each block
-//     recomputes its TS+1 states from the checkpoint, then walks backwards:
-//       lam  += C_t g_t                       (g_t = dy_t silu(z_t))
-//       dx    = delta sum_n lam B + D g       dB[t,n] += lam delta x (channel sum)
-//       dC[t,n] += g h_t                       ddelta = sum_n lam (A a h_{t-1} + B x)
-//       dA[n] += lam a h_{t-1} delta           lam <- lam a
+//     recomputes its TS states (and delta, sigmoid(u)) from the checkpoint,
+//     then walks backwards:
+//       lam  += C_t g_t                        (g_t = dy_t silu(z_t), lam = dL/dh_t)
+//       dx    = delta sum_n lam B + D g        dB[t,n] = sum_d lam delta x
+//       dC[t,n] = sum_d g h_t                   ddelta = sum_n lam (A a h_{t-1} + B x)
+//       dA[n] += lam a h_{t-1} delta            lam <- lam a
+//     dB/dC: each lane writes its 32 products to an LDS row; lane q of the
+//     wave sums column (q mod 32) over half of the 64 rows; the 2 halves x 4
+//     waves are summed after the block and written as one partial per
+//     (token, workgroup).
 template <typename T, bool GATE>
 __global__ __launch_bounds__(WG) void k_bwd_main(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
@@ -400,8 +400,9 @@ __global__ __launch_bounds__(WG) void k_bwd_main(
     T* __restrict__ dzo, float* __restrict__ dh0, float* __restrict__ wsBC,
     float* __restrict__ wsPA, float* __restrict__ wsPD, int L, int D, int Tc, int K,
     int64_t nck, int ndb) {
-    __shared__ float scr[NWAVE][64 * 36];
-    __shared__ float wres[NWAVE][TS][32];
+    constexpr int RS = 36;  // LDS row stride in floats: 16-byte aligned rows
+    __shared__ float rows[NWAVE][64 * RS];
+    __shared__ float wres[TS][2 * NWAVE][32];
     const int d = blockIdx.x * WG + threadIdx.x;
     const int k = blockIdx.y;
     const int b = blockIdx.z;
@@ -421,45 +422,45 @@ __global__ __launch_bounds__(WG) void k_bwd_main(
 #pragma unroll
     for (int n = 0; n < NS; ++n) dA[n] = 0.0f;
     float dDacc = 0.0f, ddtbacc = 0.0f;
+    float* myrow = rows[wave] + lane * RS;
+    const int col = lane & 31, half = lane >> 5;
+    const float* colp = rows[wave] + (half * 32) * RS + col;
     const int t0 = k * Tc, t1 = min(t0 + Tc, L);
     const int j0 = t0 / TS, j1 = (t1 + TS - 1) / TS;
     for (int j = j1 - 1; j >= j0; --j) {
         const int ts = j * TS;
         const int cnt = min(TS, t1 - ts);
         const int64_t row0 = (int64_t)b * L + ts;
-        float hc[TS + 1][NS];
-        load_state(ckpt + (((int64_t)b * nck + j) * D + dc) * NS, hc[0]);
-        // recompute the block's states
+        const float* ckp = ckpt + (((int64_t)b * nck + j) * D + dc) * NS;
+        float hc[TS][NS];  // state after token ts+i
+        {
+            float hs[NS];
+            load_state(ckp, hs);
 #pragma unroll
-        for (int i = 0; i < TS; ++i) {
-            if (i < cnt) {
-                const int64_t row = row0 + i;
-                const float xv = to_f(x[row * D + dc]), dtv = to_f(dt[row * D + dc]);
-                float Bv[NS];
-                load16(Bm + row * NS, Bv);
-                float sg;
-                const float delta = softplus_sig(dtv + bias, sg);
-                const float dxv = delta * xv;
+            for (int i = 0; i < TS; ++i) {
+                if (i < cnt) {
+                    const int64_t row = row0 + i;
+                    const float xv = to_f(x[row * D + dc]), dtv = to_f(dt[row * D + dc]);
+                    float Bv[NS];
+                    load16(Bm + row * NS, Bv);
+                    float sg;
+                    const float delta = softplus_sig(dtv + bias, sg);
+                    const float dxv = delta * xv;
 #pragma unroll
-                for (int n = 0; n < NS; ++n) {
-                    const float a = __builtin_amdgcn_exp2f(delta * A2[n]);
-                    hc[i + 1][n] = __builtin_fmaf(a, hc[i][n], dxv * Bv[n]);
+                    for (int n = 0; n < NS; ++n) {
+                        const float a = __builtin_amdgcn_exp2f(delta * A2[n]);
+                        hc[i][n] = __builtin_fmaf(a, i ? hc[i - 1][n] : hs[n], dxv * Bv[n]);
+                    }
                 }
             }
         }
-        // reverse sweep
 #pragma unroll
         for (int i = TS - 1; i >= 0; --i) {
             if (i < cnt) {
                 const int64_t row = row0 + i;
-                const float xv = to_f(x[row * D + dc]), dtv = to_f(dt[row * D + dc]);
+                const float xv = to_f(x[row * D + dc]);
+                const float dtv = to_f(dt[row * D + dc]);
                 const float dyv = to_f(dy[row * D + dc]);
-                float Bv[NS], Cv[NS];
-                load16(Bm + row * NS, Bv);
-                load16(Cm + row * NS, Cv);
-                float sg;
-                const float delta = softplus_sig(dtv + bias, sg);
-                const float dxv = delta * xv;
                 float zv = 0.0f, sz = 0.0f, g = dyv;
                 if (GATE) {
                     zv = to_f(z[row * D + dc]);
@@ -467,26 +468,55 @@ __global__ __launch_bounds__(WG) void k_bwd_main(
                     g = dyv * (zv * sz);
                 }
                 if (!act) g = 0.0f;
+                float Bv[NS], Cv[NS];
+                load16(Bm + row * NS, Bv);
+                load16(Cm + row * NS, Cv);
+                float sgu;
+                const float delta = softplus_sig(dtv + bias, sgu);
+                const float dxv = delta * xv;
+                float hp[NS];
+                if (i == 0) load_state(ckp, hp);
                 float s1 = 0.0f, s2 = 0.0f, yacc = 0.0f;
-                float dBp[NS], dCp[NS];
+                float4* r4 = reinterpret_cast<float4*>(myrow);
 #pragma unroll
-                for (int n = 0; n < NS; ++n) {
-                    const float a = __builtin_amdgcn_exp2f(delta * A2[n]);
-                    if (GATE) yacc = __builtin_fmaf(Cv[n], hc[i + 1][n], yacc);
-                    lam[n] = __builtin_fmaf(Cv[n], g, lam[n]);
-                    s1 = __builtin_fmaf(lam[n], Bv[n], s1);
-                    dBp[n] = lam[n] * dxv;
-                    dCp[n] = g * hc[i + 1][n];
-                    const float lp = lam[n] * a;
-                    const float gg = lp * hc[i][n];
-                    s2 = __builtin_fmaf(A2[n], gg, s2);
-                    dA[n] = __builtin_fmaf(delta, gg, dA[n]);
-                    lam[n] = lp;
+                for (int q = 0; q < NS / 4; ++q) {
+                    float pb[4], pc[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int n = 4 * q + m;
+                        const float a = __builtin_amdgcn_exp2f(delta * A2[n]);
+                        const float hprev = i ? hc[i - 1][n] : hp[n];
+                        if (GATE) yacc = __builtin_fmaf(Cv[n], hc[i][n], yacc);
+                        lam[n] = __builtin_fmaf(Cv[n], g, lam[n]);
+                        s1 = __builtin_fmaf(lam[n], Bv[n], s1);
+                        pb[m] = lam[n] * dxv;
+                        pc[m] = g * hc[i][n];
+                        const float lp = lam[n] * a;
+                        const float gg = lp * hprev;
+                        s2 = __builtin_fmaf(A2[n], gg, s2);
+                        dA[n] = __builtin_fmaf(delta, gg, dA[n]);
+                        lam[n] = lp;
+                    }
+                    r4[q] = make_float4(pb[0], pb[1], pb[2], pb[3]);
+                    r4[4 + q] = make_float4(pc[0], pc[1], pc[2], pc[3]);
+                }
+                // dB / dC partial sums over this wave's 64 channels
+                {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    float sacc = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 32; ++r) sacc += colp[r * RS];
+                    wres[i][2 * wave + half][col] = sacc;
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 }
                 s2 *= LN2;  // A = A2 * ln 2
                 const float dxv_out = __builtin_fmaf(delta, s1, Dd * g);
                 const float ddelta = __builtin_fmaf(xv, s1, s2);
-                const float ddtv = ddelta * sg;
+                const float ddtv = ddelta * sgu;
                 if (act) {
                     dxo[row * D + d] = from_f<T>(dxv_out);
                     ddto[row * D + d] = from_f<T>(ddtv);
@@ -498,16 +528,14 @@ __global__ __launch_bounds__(WG) void k_bwd_main(
                     dDacc = __builtin_fmaf(g, xv, dDacc);
                     ddtbacc += ddtv;
                 }
-                const float s = wave_sum32(dBp, dCp, scr[wave]);
-                if (lane < 32) wres[wave][i][lane] = s;
             }
         }
         __syncthreads();
         for (int idx = threadIdx.x; idx < cnt * 32; idx += WG) {
             const int i = idx >> 5, v = idx & 31;
-            float s = wres[0][i][v];
+            float s = wres[i][0][v];
 #pragma unroll
-            for (int w = 1; w < NWAVE; ++w) s += wres[w][i][v];
+            for (int w = 1; w < 2 * NWAVE; ++w) s += wres[i][w][v];
             wsBC[((row0 + i) * ndb + blockIdx.x) * 32 + v] = s;
         }
         __syncthreads();
