@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--cpu-sample-channels", type=int, default=0,
                     help="channels the oracle baseline runs on (0 = all)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (known bytes) to calibrate "
+                         "profiler FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -111,6 +114,12 @@ def main():
         ssm.ssm_scan_bwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"], ckpt,
                          t["dy"], out=grads, timing=timer)
 
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

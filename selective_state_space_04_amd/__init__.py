@@ -19,7 +19,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+# SSM_SCAN_LIB may point at another build of the same library (A/B timing).
+LIB_PATH = os.environ.get("SSM_SCAN_LIB") or os.path.join(_HERE, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 D_STATE = 16

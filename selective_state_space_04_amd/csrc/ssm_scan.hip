@@ -46,6 +46,11 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int64_t TARGET_LANES = 262144;  // 4096 waves = 4 per SIMD
 constexpr int64_t MIN_CHUNK = 64;
+constexpr int64_t NUM_CU = 256;
+// Resident workgroups of the forward main kernel (7 waves/SIMD at its register
+// count) and of the backward main kernel (2 waves/SIMD), chip-wide.
+constexpr int64_t FWD_SLOTS = NUM_CU * 7;
+constexpr int64_t BWD_SLOTS = NUM_CU * 2;
 
 typedef uint16_t bf16_t;
 
@@ -186,13 +191,17 @@ __global__ __launch_bounds__(WG) void k_fwd_chunk(
     const Stream<T> xs{x + row0 * D + dc, D}, ds{dt + row0 * D + dc, D};
     const T* bp = Bm + row0 * NS;
     float xn = xs.at(0), dn = ds.at(0);
+    float Bn[NS];
+    load16(bp, Bn);
     for (int i = 0; i < nt; ++i) {
         const float xv = xn, dtv = dn;
         const int ip = min(i + 1, nt - 1);
         xn = xs.at(ip);
         dn = ds.at(ip);
         float Bv[NS];
-        load16(bp + (int64_t)i * NS, Bv);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) Bv[n] = Bn[n];
+        load16(bp + (int64_t)ip * NS, Bn);  // next token's row (scalar cache)
         float sg;
         const float delta = softplus_sig(dtv + bias, sg);
         const float dxv = delta * xv;
@@ -278,6 +287,9 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
     float* ck = ckpt ? ckpt + (((int64_t)b * nck + t0 / TS) * D + d) * NS : nullptr;
     const int64_t ckstride = (int64_t)D * NS;
     float xn = xs.at(0), dn = ds.at(0), zn = GATE ? zs.at(0) : 0.0f;
+    float Bn[NS], Cn[NS];
+    load16(bp, Bn);
+    load16(cp, Cn);
     for (int i = 0; i < nt; ++i) {
         // checkpoint: state before token t0+i (chunk starts k>0 come from the carry kernel)
         if ((i & (TS - 1)) == 0 && ck && act && (i > 0 || k == 0))
@@ -288,8 +300,13 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
         dn = ds.at(ip);
         if (GATE) zn = zs.at(ip);
         float Bv[NS], Cv[NS];
-        load16(bp + (int64_t)i * NS, Bv);
-        load16(cp + (int64_t)i * NS, Cv);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            Bv[n] = Bn[n];
+            Cv[n] = Cn[n];
+        }
+        load16(bp + (int64_t)ip * NS, Bn);  // next token's rows (scalar cache)
+        load16(cp + (int64_t)ip * NS, Cn);
         float sg;
         const float delta = softplus_sig(dtv + bias, sg);
         const float acc = scan_token(h, A2, Bv, Cv, delta, xv);
@@ -326,6 +343,8 @@ __global__ __launch_bounds__(WG) void k_bwd_chunk(
     const Stream<T> zs{GATE ? z + row0 * D + dc : nullptr, D};
     const T* cp = Cm + row0 * NS;
     float dn = ds.at(nt - 1), gn = gs.at(nt - 1), zn = GATE ? zs.at(nt - 1) : 0.0f;
+    float Cn[NS];
+    load16(cp + (int64_t)(nt - 1) * NS, Cn);
     for (int i = nt - 1; i >= 0; --i) {
         const float dtv = dn, dyv = gn, zv = zn;
         const int ip = max(i - 1, 0);
@@ -334,7 +353,9 @@ __global__ __launch_bounds__(WG) void k_bwd_chunk(
         if (GATE) zn = zs.at(ip);
         const float g = GATE ? dyv * (zv * sigmoid_f(zv)) : dyv;
         float Cv[NS];
-        load16(cp + (int64_t)i * NS, Cv);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) Cv[n] = Cn[n];
+        load16(cp + (int64_t)ip * NS, Cn);  // next token's row (scalar cache)
         float sg;
         const float delta = softplus_sig(dtv + bias, sg);
 #pragma unroll
@@ -632,7 +653,9 @@ __global__ __launch_bounds__(WG) void k_fill(float* __restrict__ dst, const floa
 struct Plan {
     int64_t Bt, L, D;
     int io;
-    int64_t Tc, K, nck, ndb;
+    int64_t Tf, Kf;  // forward chunk length / count
+    int64_t Tb, Kb;  // backward chunk length / count
+    int64_t nck, ndb;
 };
 
 ssm_status check_dims(const ssm_dims* d) {
@@ -646,24 +669,53 @@ ssm_status check_dims(const ssm_dims* d) {
     return SSM_OK;
 }
 
+// Chunk length (a multiple of TS) for a kernel launched as one workgroup per
+// (channel block, chunk, batch row), `wg_per_chunk` workgroups per chunk, with
+// `slots` workgroups resident on the chip at once.  Picks the chunk count that
+// fills whole rounds of resident workgroups best (the last round of a launch
+// otherwise runs partly empty), among counts that fill the chip at least once;
+// ties go to fewer chunks.  Tiny problems take as many chunks as allowed.
+int64_t pick_chunk(int64_t L, int64_t wg_per_chunk, int64_t slots) {
+    const int64_t kmax = std::max<int64_t>(1, std::min<int64_t>(L / MIN_CHUNK, 4096));
+    int64_t best_tc = -1;
+    double best_eff = -1.0;
+    int64_t prev_k = -1;
+    for (int64_t kt = 1; kt <= kmax; ++kt) {
+        int64_t tc = (L + kt - 1) / kt;
+        tc = (tc + TS - 1) / TS * TS;
+        const int64_t k = (L + tc - 1) / tc;
+        if (k == prev_k) continue;
+        prev_k = k;
+        const int64_t w = wg_per_chunk * k;
+        if (w < slots && kt < kmax) continue;
+        const int64_t rounds = (w + slots - 1) / slots;
+        const double eff = (double)w / (double)(rounds * slots);
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best_tc = tc;
+        }
+    }
+    if (best_tc < 0) best_tc = (L + TS - 1) / TS * TS;
+    return std::max<int64_t>(best_tc, TS);
+}
+
 Plan make_plan(const ssm_dims* d) {
     Plan p;
     p.Bt = d->batch;
     p.L = d->seqlen;
     p.D = d->d_inner;
     p.io = d->io_dtype;
-    const int64_t lanes = p.Bt * p.D;
-    int64_t kt = (TARGET_LANES + lanes - 1) / lanes;
-    kt = std::min<int64_t>(kt, p.L / MIN_CHUNK);
-    kt = std::min<int64_t>(kt, 4096);  // grid.y limit with margin
-    if (kt < 1) kt = 1;
-    int64_t tc = (p.L + kt - 1) / kt;
-    tc = (tc + TS - 1) / TS * TS;
-    if (tc < TS) tc = TS;
-    p.Tc = tc;
-    p.K = p.L > 0 ? (p.L + tc - 1) / tc : 1;
     p.nck = (p.L + TS - 1) / TS;
     p.ndb = (p.D + WG - 1) / WG;
+    const int64_t Lp = std::max<int64_t>(p.L, 1);
+    // Forward: one chunk (a purely sequential scan, same operation order as the
+    // single-token step) when the channels alone fill the chip or the sequence
+    // is short.
+    if (p.Bt * p.D >= TARGET_LANES || p.L < 2 * MIN_CHUNK) p.Tf = (Lp + TS - 1) / TS * TS;
+    else p.Tf = pick_chunk(p.L, p.Bt * p.ndb, FWD_SLOTS);
+    p.Kf = (Lp + p.Tf - 1) / p.Tf;
+    p.Tb = p.L < 2 * MIN_CHUNK ? (Lp + TS - 1) / TS * TS : pick_chunk(p.L, p.Bt * p.ndb, BWD_SLOTS);
+    p.Kb = (Lp + p.Tb - 1) / p.Tb;
     return p;
 }
 
@@ -674,11 +726,11 @@ struct FwdWs {
 };
 FwdWs fwd_ws(const Plan& p) {
     FwdWs w{0, 0, 0, 0};
-    if (p.K > 1) {
+    if (p.Kf > 1) {
         w.S = 0;
-        w.sum = w.S + align_up(sizeof(float) * p.Bt * (p.K - 1) * p.D * NS);
-        w.starts = w.sum + align_up(sizeof(float) * p.Bt * (p.K - 1) * p.D);
-        w.total = w.starts + align_up(sizeof(float) * p.Bt * p.K * p.D * NS);
+        w.sum = w.S + align_up(sizeof(float) * p.Bt * (p.Kf - 1) * p.D * NS);
+        w.starts = w.sum + align_up(sizeof(float) * p.Bt * (p.Kf - 1) * p.D);
+        w.total = w.starts + align_up(sizeof(float) * p.Bt * p.Kf * p.D * NS);
     }
     return w;
 }
@@ -689,14 +741,14 @@ struct BwdWs {
 BwdWs bwd_ws(const Plan& p) {
     BwdWs w{};
     size_t off = 0;
-    if (p.K > 1) {
-        w.G = off; off += align_up(sizeof(float) * p.Bt * (p.K - 1) * p.D * NS);
-        w.sum = off; off += align_up(sizeof(float) * p.Bt * (p.K - 1) * p.D);
-        w.X = off; off += align_up(sizeof(float) * p.Bt * p.K * p.D * NS);
+    if (p.Kb > 1) {
+        w.G = off; off += align_up(sizeof(float) * p.Bt * (p.Kb - 1) * p.D * NS);
+        w.sum = off; off += align_up(sizeof(float) * p.Bt * (p.Kb - 1) * p.D);
+        w.X = off; off += align_up(sizeof(float) * p.Bt * p.Kb * p.D * NS);
     }
     w.BC = off; off += align_up(sizeof(float) * p.Bt * p.L * p.ndb * 32);
-    w.PA = off; off += align_up(sizeof(float) * p.Bt * p.K * p.D * NS);
-    w.PD = off; off += align_up(sizeof(float) * p.Bt * p.K * p.D * 2);
+    w.PA = off; off += align_up(sizeof(float) * p.Bt * p.Kb * p.D * NS);
+    w.PD = off; off += align_up(sizeof(float) * p.Bt * p.Kb * p.D * 2);
     w.total = off;
     return w;
 }
@@ -734,27 +786,27 @@ ssm_status run_fwd(const Plan& p, const void* x, const void* dt, const void* B, 
                    Launcher& launch) {
     const FwdWs w = fwd_ws(p);
     char* wsb = static_cast<char*>(ws);
-    float* S = p.K > 1 ? reinterpret_cast<float*>(wsb + w.S) : nullptr;
-    float* sum = p.K > 1 ? reinterpret_cast<float*>(wsb + w.sum) : nullptr;
+    float* S = p.Kf > 1 ? reinterpret_cast<float*>(wsb + w.S) : nullptr;
+    float* sum = p.Kf > 1 ? reinterpret_cast<float*>(wsb + w.sum) : nullptr;
     float* starts;
     int64_t nent, kstep;
     if (ckpt) {
         starts = ckpt;
         nent = p.nck;
-        kstep = p.Tc / TS;
+        kstep = p.Tf / TS;
     } else {
-        starts = p.K > 1 ? reinterpret_cast<float*>(wsb + w.starts) : nullptr;
-        nent = p.K;
+        starts = p.Kf > 1 ? reinterpret_cast<float*>(wsb + w.starts) : nullptr;
+        nent = p.Kf;
         kstep = 1;
     }
-    const int L = (int)p.L, D = (int)p.D, Tc = (int)p.Tc, K = (int)p.K;
-    if (p.K > 1) {
-        SSM_TRY(launch(SSM_K_FWD_CHUNK, k_fwd_chunk<T>, dim3(p.ndb, p.K - 1, p.Bt),
+    const int L = (int)p.L, D = (int)p.D, Tc = (int)p.Tf, K = (int)p.Kf;
+    if (p.Kf > 1) {
+        SSM_TRY(launch(SSM_K_FWD_CHUNK, k_fwd_chunk<T>, dim3(p.ndb, p.Kf - 1, p.Bt),
                        (const T*)x, (const T*)dt, (const T*)B, A_log, dt_bias, S, sum, L, D, Tc, K));
         SSM_TRY(launch(SSM_K_FWD_CARRY, k_fwd_carry, dim3(p.ndb, 1, p.Bt), A_log, h0,
                        (const float*)S, (const float*)sum, starts, D, K, nent, kstep));
     }
-    return launch(SSM_K_FWD_MAIN, k_fwd_main<T, GATE>, dim3(p.ndb, p.K, p.Bt), (const T*)x,
+    return launch(SSM_K_FWD_MAIN, k_fwd_main<T, GATE>, dim3(p.ndb, p.Kf, p.Bt), (const T*)x,
                   (const T*)dt, (const T*)B, (const T*)C, (const T*)z, A_log, Dp, dt_bias, h0,
                   (const float*)starts, (T*)y, h_last, ckpt, L, D, Tc, K, (int64_t)p.nck, nent,
                   kstep);
@@ -768,21 +820,21 @@ ssm_status run_bwd(const Plan& p, const void* x, const void* dt, const void* B, 
                    Launcher& launch) {
     const BwdWs w = bwd_ws(p);
     char* wsb = static_cast<char*>(ws);
-    float* G = p.K > 1 ? reinterpret_cast<float*>(wsb + w.G) : nullptr;
-    float* sum = p.K > 1 ? reinterpret_cast<float*>(wsb + w.sum) : nullptr;
-    float* X = p.K > 1 ? reinterpret_cast<float*>(wsb + w.X) : nullptr;
+    float* G = p.Kb > 1 ? reinterpret_cast<float*>(wsb + w.G) : nullptr;
+    float* sum = p.Kb > 1 ? reinterpret_cast<float*>(wsb + w.sum) : nullptr;
+    float* X = p.Kb > 1 ? reinterpret_cast<float*>(wsb + w.X) : nullptr;
     float* BC = reinterpret_cast<float*>(wsb + w.BC);
     float* PA = reinterpret_cast<float*>(wsb + w.PA);
     float* PD = reinterpret_cast<float*>(wsb + w.PD);
-    const int L = (int)p.L, D = (int)p.D, Tc = (int)p.Tc, K = (int)p.K;
-    if (p.K > 1) {
-        SSM_TRY(launch(SSM_K_BWD_CHUNK, k_bwd_chunk<T, GATE>, dim3(p.ndb, p.K - 1, p.Bt),
+    const int L = (int)p.L, D = (int)p.D, Tc = (int)p.Tb, K = (int)p.Kb;
+    if (p.Kb > 1) {
+        SSM_TRY(launch(SSM_K_BWD_CHUNK, k_bwd_chunk<T, GATE>, dim3(p.ndb, p.Kb - 1, p.Bt),
                        (const T*)dt, (const T*)C, (const T*)z, (const T*)dy, A_log, dt_bias, G,
                        sum, L, D, Tc, K));
         SSM_TRY(launch(SSM_K_BWD_CARRY, k_bwd_carry, dim3(p.ndb, 1, p.Bt), A_log,
                        (const float*)G, (const float*)sum, X, D, K));
     }
-    SSM_TRY(launch(SSM_K_BWD_MAIN, k_bwd_main<T, GATE>, dim3(p.ndb, p.K, p.Bt), (const T*)x,
+    SSM_TRY(launch(SSM_K_BWD_MAIN, k_bwd_main<T, GATE>, dim3(p.ndb, p.Kb, p.Bt), (const T*)x,
                    (const T*)dt, (const T*)B, (const T*)C, (const T*)z, (const T*)dy, A_log, Dp,
                    dt_bias, ckpt, (const float*)X, (T*)dx, (T*)ddt, (T*)dz, dh0, BC, PA, PD, L,
                    D, Tc, K, (int64_t)p.nck, (int)p.ndb));
@@ -792,7 +844,7 @@ ssm_status run_bwd(const Plan& p, const void* x, const void* dt, const void* B, 
     const int64_t np = p.D * NS + p.D;
     return launch(SSM_K_BWD_REDUCE_P, k_bwd_reduce_params, dim3((unsigned)((np + WG - 1) / WG)),
                   A_log, (const float*)PA, (const float*)PD, dA_log, dD, ddt_bias, (int)p.Bt,
-                  (int)p.K, D);
+                  (int)p.Kb, D);
 }
 
 }  // namespace
