@@ -60,11 +60,9 @@ __device__ __forceinline__ float to_f(bf16_t v) { return __uint_as_float((uint32
 
 template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+// f32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) {
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                                           // nearest even
-    return (bf16_t)(u >> 16);
+    return __builtin_bit_cast(bf16_t, (__bf16)v);
 }
 
 // 16 consecutive values (one B_t or C_t row); the address is wave-uniform.
@@ -412,7 +410,7 @@ __global__ __launch_bounds__(WG) void k_bwd_carry(
 //     waves are summed after the block and written as one partial per
 //     (token, workgroup).
 template <typename T, bool GATE>
-__global__ __launch_bounds__(WG) void k_bwd_main(
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_main(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const T* __restrict__ z, const T* __restrict__ dy,
     const float* __restrict__ A_log, const float* __restrict__ Dp,
@@ -424,6 +422,7 @@ __global__ __launch_bounds__(WG) void k_bwd_main(
     constexpr int RS = 36;  // LDS row stride in floats: 16-byte aligned rows
     __shared__ float rows[NWAVE][64 * RS];
     __shared__ float wres[TS][2 * NWAVE][32];
+    __shared__ float2 dsg[NWAVE][TS][64];  // per token: delta, sigmoid(dt + dt_bias)
     const int d = blockIdx.x * WG + threadIdx.x;
     const int k = blockIdx.y;
     const int b = blockIdx.z;
@@ -466,6 +465,7 @@ __global__ __launch_bounds__(WG) void k_bwd_main(
                     load16(Bm + row * NS, Bv);
                     float sg;
                     const float delta = softplus_sig(dtv + bias, sg);
+                    dsg[wave][i][lane] = make_float2(delta, sg);
                     const float dxv = delta * xv;
 #pragma unroll
                     for (int n = 0; n < NS; ++n) {
@@ -475,16 +475,31 @@ __global__ __launch_bounds__(WG) void k_bwd_main(
                 }
             }
         }
+        // Activations of the next (earlier) token are fetched before this token's
+        // stores are issued: loads and stores retire in order, so a load issued
+        // after a store would also wait for that store.
+        T xn, gn, zn = T(0);
+        {
+            const int64_t rl = (row0 + cnt - 1) * D + dc;
+            xn = x[rl];
+            gn = dy[rl];
+            if (GATE) zn = z[rl];
+        }
 #pragma unroll
         for (int i = TS - 1; i >= 0; --i) {
             if (i < cnt) {
                 const int64_t row = row0 + i;
-                const float xv = to_f(x[row * D + dc]);
-                const float dtv = to_f(dt[row * D + dc]);
-                const float dyv = to_f(dy[row * D + dc]);
+                const float xv = to_f(xn);
+                const float dyv = to_f(gn);
                 float zv = 0.0f, sz = 0.0f, g = dyv;
+                if (GATE) zv = to_f(zn);
+                if (i > 0) {
+                    const int64_t rp = (row - 1) * D + dc;
+                    xn = x[rp];
+                    gn = dy[rp];
+                    if (GATE) zn = z[rp];
+                }
                 if (GATE) {
-                    zv = to_f(z[row * D + dc]);
                     sz = sigmoid_f(zv);
                     g = dyv * (zv * sz);
                 }
@@ -492,8 +507,8 @@ __global__ __launch_bounds__(WG) void k_bwd_main(
                 float Bv[NS], Cv[NS];
                 load16(Bm + row * NS, Bv);
                 load16(Cm + row * NS, Cv);
-                float sgu;
-                const float delta = softplus_sig(dtv + bias, sgu);
+                const float2 ds = dsg[wave][i][lane];
+                const float delta = ds.x, sgu = ds.y;
                 const float dxv = delta * xv;
                 float hp[NS];
                 if (i == 0) load_state(ckp, hp);

@@ -340,3 +340,17 @@ def test_step_bf16_matches_forward():
     torch.cuda.synchronize()
     assert torch.equal(torch.stack(ys, 1), y)
     assert torch.equal(hs, h)
+
+
+def test_bf16_outputs_are_nearest_even_roundings_of_the_f32_path():
+    """With bf16-representable inputs the bf16-I/O kernels do the same f32
+    arithmetic as the f32-I/O kernels; every stored bf16 output must be the
+    round-to-nearest-even of the corresponding f32 result, bit for bit."""
+    inp = W.make_inputs(2, 300, 200, seed=22, bf16=True)
+    y32, _, g32 = _gpu_fwd_bwd(inp, io=torch.float32)
+    y16, _, g16 = _gpu_fwd_bwd(inp, io=torch.bfloat16)
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+    for k in ("dx", "ddt", "dz", "dB", "dC"):
+        assert torch.equal(g16[k], g32[k].to(torch.bfloat16)), k
+    for k in ("dA_log", "dD", "ddt_bias"):
+        assert torch.equal(g16[k], g32[k]), k
