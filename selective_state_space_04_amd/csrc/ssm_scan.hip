@@ -162,7 +162,12 @@ struct Stream {
     const T* p;
     int64_t stride;
     __device__ __forceinline__ float at(int i) const { return to_f(p[(int64_t)i * stride]); }
+    __device__ __forceinline__ T raw(int i) const { return p[(int64_t)i * stride]; }
 };
+
+// Per-lane loads run PF tokens ahead of use (a ring of raw values; the token
+// loop is unrolled PF times so the ring rotation is register renaming).
+constexpr int PF = 3;
 
 // ===================================================================== forward
 
@@ -188,14 +193,25 @@ __global__ __launch_bounds__(WG) void k_fwd_chunk(
     const int64_t row0 = (int64_t)b * L + t0;
     const Stream<T> xs{x + row0 * D + dc, D}, ds{dt + row0 * D + dc, D};
     const T* bp = Bm + row0 * NS;
-    float xn = xs.at(0), dn = ds.at(0);
+    T xq[PF], dq[PF];
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+        xq[q] = xs.raw(min(q, nt - 1));
+        dq[q] = ds.raw(min(q, nt - 1));
+    }
     float Bn[NS];
     load16(bp, Bn);
+#pragma unroll PF
     for (int i = 0; i < nt; ++i) {
-        const float xv = xn, dtv = dn;
+        const float xv = to_f(xq[0]), dtv = to_f(dq[0]);
+#pragma unroll
+        for (int q = 0; q + 1 < PF; ++q) {
+            xq[q] = xq[q + 1];
+            dq[q] = dq[q + 1];
+        }
+        xq[PF - 1] = xs.raw(min(i + PF, nt - 1));
+        dq[PF - 1] = ds.raw(min(i + PF, nt - 1));
         const int ip = min(i + 1, nt - 1);
-        xn = xs.at(ip);
-        dn = ds.at(ip);
         float Bv[NS];
 #pragma unroll
         for (int n = 0; n < NS; ++n) Bv[n] = Bn[n];
@@ -284,19 +300,32 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
     T* yp = y + row0 * D + d;
     float* ck = ckpt ? ckpt + (((int64_t)b * nck + t0 / TS) * D + d) * NS : nullptr;
     const int64_t ckstride = (int64_t)D * NS;
-    float xn = xs.at(0), dn = ds.at(0), zn = GATE ? zs.at(0) : 0.0f;
+    T xq[PF], dq[PF], zq[PF];
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+        xq[q] = xs.raw(min(q, nt - 1));
+        dq[q] = ds.raw(min(q, nt - 1));
+        zq[q] = GATE ? zs.raw(min(q, nt - 1)) : T(0);
+    }
     float Bn[NS], Cn[NS];
     load16(bp, Bn);
     load16(cp, Cn);
+#pragma unroll PF
     for (int i = 0; i < nt; ++i) {
         // checkpoint: state before token t0+i (chunk starts k>0 come from the carry kernel)
         if ((i & (TS - 1)) == 0 && ck && act && (i > 0 || k == 0))
             store_state(ck + (int64_t)(i / TS) * ckstride, h);
-        const float xv = xn, dtv = dn, zv = zn;
+        const float xv = to_f(xq[0]), dtv = to_f(dq[0]), zv = GATE ? to_f(zq[0]) : 0.0f;
+#pragma unroll
+        for (int q = 0; q + 1 < PF; ++q) {
+            xq[q] = xq[q + 1];
+            dq[q] = dq[q + 1];
+            zq[q] = zq[q + 1];
+        }
+        xq[PF - 1] = xs.raw(min(i + PF, nt - 1));
+        dq[PF - 1] = ds.raw(min(i + PF, nt - 1));
+        if (GATE) zq[PF - 1] = zs.raw(min(i + PF, nt - 1));
         const int ip = min(i + 1, nt - 1);
-        xn = xs.at(ip);
-        dn = ds.at(ip);
-        if (GATE) zn = zs.at(ip);
         float Bv[NS], Cv[NS];
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
@@ -340,15 +369,28 @@ __global__ __launch_bounds__(WG) void k_bwd_chunk(
     const Stream<T> ds{dt + row0 * D + dc, D}, gs{dy + row0 * D + dc, D};
     const Stream<T> zs{GATE ? z + row0 * D + dc : nullptr, D};
     const T* cp = Cm + row0 * NS;
-    float dn = ds.at(nt - 1), gn = gs.at(nt - 1), zn = GATE ? zs.at(nt - 1) : 0.0f;
+    T dq[PF], gq[PF], zq[PF];
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+        dq[q] = ds.raw(max(nt - 1 - q, 0));
+        gq[q] = gs.raw(max(nt - 1 - q, 0));
+        zq[q] = GATE ? zs.raw(max(nt - 1 - q, 0)) : T(0);
+    }
     float Cn[NS];
     load16(cp + (int64_t)(nt - 1) * NS, Cn);
+#pragma unroll PF
     for (int i = nt - 1; i >= 0; --i) {
-        const float dtv = dn, dyv = gn, zv = zn;
+        const float dtv = to_f(dq[0]), dyv = to_f(gq[0]), zv = GATE ? to_f(zq[0]) : 0.0f;
+#pragma unroll
+        for (int q = 0; q + 1 < PF; ++q) {
+            dq[q] = dq[q + 1];
+            gq[q] = gq[q + 1];
+            zq[q] = zq[q + 1];
+        }
+        dq[PF - 1] = ds.raw(max(i - PF, 0));
+        gq[PF - 1] = gs.raw(max(i - PF, 0));
+        if (GATE) zq[PF - 1] = zs.raw(max(i - PF, 0));
         const int ip = max(i - 1, 0);
-        dn = ds.at(ip);
-        gn = gs.at(ip);
-        if (GATE) zn = zs.at(ip);
         const float g = GATE ? dyv * (zv * sigmoid_f(zv)) : dyv;
         float Cv[NS];
 #pragma unroll
@@ -453,14 +495,27 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int64_t row0 = (int64_t)b * L + ts;
         const float* ckp = ckpt + (((int64_t)b * nck + j) * D + dc) * NS;
         float hc[TS][NS];  // state after token ts+i
+        // first token of the reverse sweep, fetched early
+        T xn, gn, zn = T(0);
+        {
+            const int64_t rl = (row0 + cnt - 1) * D + dc;
+            xn = x[rl];
+            gn = dy[rl];
+            if (GATE) zn = z[rl];
+        }
         {
             float hs[NS];
             load_state(ckp, hs);
+            T xr = x[row0 * D + dc], dr = dt[row0 * D + dc];
 #pragma unroll
             for (int i = 0; i < TS; ++i) {
                 if (i < cnt) {
                     const int64_t row = row0 + i;
-                    const float xv = to_f(x[row * D + dc]), dtv = to_f(dt[row * D + dc]);
+                    const float xv = to_f(xr), dtv = to_f(dr);
+                    if (i + 1 < cnt) {  // next token, one ahead
+                        xr = x[(row + 1) * D + dc];
+                        dr = dt[(row + 1) * D + dc];
+                    }
                     float Bv[NS];
                     load16(Bm + row * NS, Bv);
                     float sg;
@@ -478,13 +533,6 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         // Activations of the next (earlier) token are fetched before this token's
         // stores are issued: loads and stores retire in order, so a load issued
         // after a store would also wait for that store.
-        T xn, gn, zn = T(0);
-        {
-            const int64_t rl = (row0 + cnt - 1) * D + dc;
-            xn = x[rl];
-            gn = dy[rl];
-            if (GATE) zn = z[rl];
-        }
 #pragma unroll
         for (int i = TS - 1; i >= 0; --i) {
             if (i < cnt) {
