@@ -104,9 +104,17 @@ __device__ __forceinline__ void store_state(float* __restrict__ p, const float h
 
 // ---------------------------------------------------------------- token math
 // A2[n] = A[n] * log2(e) with A = -exp(A_log), so exp(delta*A) = exp2(delta*A2).
+// exp(A_log) is one v_exp_f32 of A_log*log2(e) (about 2e-7 relative).
 __device__ __forceinline__ void load_A2(const float* __restrict__ A_log, int d, float A2[NS]) {
+    const float4* p = reinterpret_cast<const float4*>(A_log + (int64_t)d * NS);
 #pragma unroll
-    for (int n = 0; n < NS; ++n) A2[n] = -expf(A_log[(int64_t)d * NS + n]) * LOG2E;
+    for (int i = 0; i < NS / 4; ++i) {
+        const float4 v = p[i];
+        A2[4 * i + 0] = -__builtin_amdgcn_exp2f(v.x * LOG2E) * LOG2E;
+        A2[4 * i + 1] = -__builtin_amdgcn_exp2f(v.y * LOG2E) * LOG2E;
+        A2[4 * i + 2] = -__builtin_amdgcn_exp2f(v.z * LOG2E) * LOG2E;
+        A2[4 * i + 3] = -__builtin_amdgcn_exp2f(v.w * LOG2E) * LOG2E;
+    }
 }
 
 // Stable softplus(u) = max(u, 0) + log1p(e), e = exp(-|u|) in (0, 1], and
@@ -676,22 +684,43 @@ __global__ __launch_bounds__(WG) void k_bwd_reduce_params(
 }
 
 // ======================================================================= step
+// One token for 256 channels of one batch row.  Each wave's 64 channels hold
+// 4 KB of contiguous state; it is moved between HBM and registers through LDS
+// so that every global load/store instruction covers 1 KB contiguously.
 template <typename T, bool GATE>
 __global__ __launch_bounds__(WG) void k_step(
     float* __restrict__ h, const T* __restrict__ x, const T* __restrict__ dt,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const T* __restrict__ z,
     const float* __restrict__ A_log, const float* __restrict__ Dp,
     const float* __restrict__ dt_bias, T* __restrict__ y, int D) {
-    const int d = blockIdx.x * WG + threadIdx.x;
+    constexpr int HS = NS + 4;  // padded LDS row (16-byte aligned, conflict-free)
+    __shared__ float hsm[NWAVE][64 * HS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int d0 = blockIdx.x * WG + wave * 64;
+    const int nvalid = min(64, D - d0);  // channels of this wave (uniform)
+    if (nvalid <= 0) return;             // no block-wide barriers below
     const int b = blockIdx.z;
-    if (d >= D) return;
+    const int d = d0 + lane;
+    const bool act = lane < nvalid;
+    float* sm = hsm[wave];
+    float4* hb = reinterpret_cast<float4*>(h + ((int64_t)b * D + d0) * NS);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int pc = j * 64 + lane;  // 16-byte piece: channel pc/4, states 4*(pc%4)..
+        if ((pc >> 2) < nvalid)
+            *reinterpret_cast<float4*>(sm + (pc >> 2) * HS + (pc & 3) * 4) = hb[pc];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int dc = act ? d : d0;
     float A2[NS];
-    load_A2(A_log, d, A2);
-    const float bias = dt_bias ? dt_bias[d] : 0.0f;
-    const float Dd = Dp ? Dp[d] : 0.0f;
-    const int64_t i = (int64_t)b * D + d;
+    load_A2(A_log, dc, A2);
+    const float bias = dt_bias ? dt_bias[dc] : 0.0f;
+    const float Dd = Dp ? Dp[dc] : 0.0f;
+    const int64_t i = (int64_t)b * D + dc;
     float hs[NS];
-    load_state(h + i * NS, hs);
+    load_state(sm + (act ? lane : 0) * HS, hs);
     float Bv[NS], Cv[NS];
     load16(Bm + (int64_t)b * NS, Bv);
     load16(Cm + (int64_t)b * NS, Cv);
@@ -700,8 +729,19 @@ __global__ __launch_bounds__(WG) void k_step(
     float sg;
     const float delta = softplus_sig(dtv + bias, sg);
     const float acc = scan_token(hs, A2, Bv, Cv, delta, xv);
-    y[i] = from_f<T>(finish_y<GATE>(acc, Dd, xv, zv));
-    store_state(h + i * NS, hs);
+    if (act) {
+        y[i] = from_f<T>(finish_y<GATE>(acc, Dd, xv, zv));
+        store_state(sm + lane * HS, hs);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int pc = j * 64 + lane;
+        if ((pc >> 2) < nvalid)
+            hb[pc] = *reinterpret_cast<const float4*>(sm + (pc >> 2) * HS + (pc & 3) * 4);
+    }
 }
 
 // Fills used when seqlen == 0: dst[i] = src ? src[i] : 0.
