@@ -7,10 +7,16 @@ synthetic tensors already resident in HBM.  The metric is elements
 (batch*seqlen*d_inner*d_state) per second.
 
 Prints ONE JSON line.  Besides the contract fields it carries
-  roofline      : the dominant kernel's algorithmic bytes per launch / its
-                  average launch time (HIP events recorded by the library around
-                  each launch on the launch stream), against 8 TB/s HBM;
+  roofline      : the dominant kernel against the bound that limits it, the f32
+                  vector ALU: its algorithmic flops per launch / its average
+                  launch time (HIP events recorded by the library around each
+                  launch on the launch stream), against 157.3 TFLOP/s;
+  roofline_hbm  : the same kernel's algorithmic bytes per launch / launch time,
+                  against 8 TB/s HBM;
   cpu_baseline  : the f64 oracle timed on a bounded sample on the host cores.
+The measured HBM traffic of the dominant kernel (profiler byte counters, scaled
+by a plain copy of known size) is taken from profiles/ when it was recorded for
+the current kernel source, else null.
 """
 import argparse
 import json
@@ -23,6 +29,18 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+F32_VECTOR_PEAK_TFLOPS = 157.3
+KERNEL_SRC = os.path.join(ROOT, "selective_state_space_04_amd", "csrc", "ssm_scan.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c4_mamba2p8b_bf16_traffic.txt")
+
+# Algorithmic f32 flops per element (b,t,d,n), FMA = 2, mul/add/exp = 1.
+#  forward main : exp(dt*A) (mul + exp), dt*x*B (mul), h update (FMA), C.h (FMA)  = 7
+#  backward main: state recompute (mul + exp + mul + FMA = 5); adjoint update
+#                 (FMA), lambda.B for dx/ddelta (FMA), dB product (mul), dC product
+#                 (mul), carry lambda*a (mul), times h_prev (mul), A-term of
+#                 ddelta (FMA), dA (FMA), C.h for the gate gradient (FMA) = 14;
+#                 the two sums over channels for dB and dC (2 adds)         = 21
+FLOPS_PER_ELEMENT = {"k_fwd_main": 7, "k_bwd_main": 21}
 
 
 def parse():
@@ -32,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c4_mamba2p8b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=2,
+    ap.add_argument("--cpu-sample-rows", type=int, default=4,
                     help="batch rows the oracle baseline runs on (all tokens)")
     ap.add_argument("--cpu-sample-channels", type=int, default=0,
                     help="channels the oracle baseline runs on (0 = all)")
@@ -52,6 +70,26 @@ def algorithmic_bytes(cfg, esz):
     bwd_main = btd * esz * 7 + btn * esz * 2 + params     # x, dt, z, dy in; dx, ddt, dz out; B, C in
     bwd = bwd_main + btn * esz * 2 + params               # + dB, dC, param grads out
     return {"fwd": fwd, "bwd": bwd, "bwd_main": bwd_main, "fwd_main": fwd}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when the summary was taken on a different kernel source."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_FILE).read().split("\n")
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    kv = {}
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) >= 2 and not ln.startswith("#"):
+            kv[parts[0]] = parts[1:]
+    if kv.get("source_sha256", [None])[0] != src or kernel not in kv:
+        return None
+    f = dict(p.split("=") for p in kv[kernel])
+    return int(float(f["fetch_bytes"]) + float(f["write_bytes"]))
 
 
 def cpu_baseline(inp, cfg, rows, channels):
@@ -146,12 +184,21 @@ def main():
     ab = algorithmic_bytes(cfg, esz)
     dom_bytes = {"k_bwd_main": ab["bwd_main"], "k_fwd_main": ab["fwd_main"]}.get(dominant)
     elems = bsz * L * D * N
-    roof = None
+    roof = roof_hbm = None
     if dom_bytes is not None:
-        achieved = dom_bytes / (kavg[dominant] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dominant,
-                "kernel_ms": round(kavg[dominant], 4), "algorithmic_bytes_per_launch": dom_bytes}
+        sec = kavg[dominant] * 1e-3
+        traffic = measured_traffic(dominant)
+        flops = FLOPS_PER_ELEMENT[dominant] * elems
+        tflops = flops / sec / 1e12
+        roof = {"bound": "alu", "achieved": round(tflops, 2), "peak": F32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / F32_VECTOR_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": dominant, "kernel_ms": round(kavg[dominant], 4),
+                "algorithmic_flops_per_launch": flops, "flops_per_element": FLOPS_PER_ELEMENT[dominant]}
+        gbps = dom_bytes / sec / 1e9
+        roof_hbm = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dominant,
+                    "algorithmic_bytes_per_launch": dom_bytes,
+                    "measured_GBps": None if traffic is None else round(traffic / sec / 1e9, 1)}
     line = {
         "metric": "selective-scan fwd+bwd elements(B\u00b7L\u00b7D\u00b7N)/s and achieved HBM GB/s",
         "value": elems / (ms * 1e-3),
@@ -171,6 +218,7 @@ def main():
         "achieved_hbm_GBps": round((ab["fwd"] + ab["bwd"]) / (ms * 1e-3) / 1e9, 1),
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kavg.items())},
         "roofline": roof,
+        "roofline_hbm": roof_hbm,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
