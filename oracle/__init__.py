@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
 with the HIP library and the HIP library never calls it.
 
-The arithmetic lives in ``ssm_oracle.c`` (plain f64 loops, OpenMP over channel
-blocks).  This module only marshals numpy arrays: every input is promoted to
+The arithmetic lives in ``ssm_oracle.c`` (the scan) and ``conv_oracle.c`` (the
+causal depthwise conv1d + SiLU in front of it): plain f64 loops, OpenMP over
+channels.  This module only marshals numpy arrays: every input is promoted to
 f64 exactly (f32 and bf16 values are representable in f64) and every output is
 returned as f64.
 
@@ -43,6 +44,12 @@ def _load():
     lib.oracle_bwd.restype = ctypes.c_int
     lib.oracle_step.argtypes = [I, I, I] + [P] * 10
     lib.oracle_step.restype = ctypes.c_int
+    lib.oracle_conv_fwd.argtypes = [I, I, I, I] + [P] * 7
+    lib.oracle_conv_fwd.restype = ctypes.c_int
+    lib.oracle_conv_bwd.argtypes = [I, I, I, I] + [P] * 9
+    lib.oracle_conv_bwd.restype = ctypes.c_int
+    lib.oracle_conv_step.argtypes = [I, I, I] + [P] * 5
+    lib.oracle_conv_step.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -116,4 +123,56 @@ def step(h, x, dt, B, C, z, A_log, D, dt_bias):
     rc = _load().oracle_step(bt, d, n, _ptr(h), *[_ptr(a) for a in args], _ptr(y))
     if rc != 0:
         raise RuntimeError(f"oracle_step failed: {rc}")
+    return y
+
+
+def _conv_dims(x, w):
+    x = np.asarray(x)
+    w = np.asarray(w)
+    if x.ndim != 3 or w.ndim != 2 or w.shape[0] != x.shape[2]:
+        raise ValueError("x must be [batch, seqlen, d_inner] and w [d_inner, d_conv]")
+    return x.shape[0], x.shape[1], x.shape[2], w.shape[1]
+
+
+def conv_fwd(x, w, bias, s0=None):
+    """Causal depthwise conv1d + SiLU.  Returns dict(y, pre, s_last), all f64:
+    y = silu(pre) [batch, L, d_inner]; s_last [batch, d_inner, d_conv-1] the last
+    d_conv-1 inputs, oldest first (from s0 when L < d_conv-1)."""
+    bt, L, d, k = _conv_dims(x, w)
+    args = [_f64(a) for a in (x, w, bias, s0)]
+    y = np.empty((bt, L, d))
+    pre = np.empty((bt, L, d))
+    s_last = np.empty((bt, d, k - 1))
+    rc = _load().oracle_conv_fwd(bt, L, d, k, *[_ptr(a) for a in args], _ptr(y), _ptr(s_last), _ptr(pre))
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv_fwd failed: {rc}")
+    return {"y": y, "pre": pre, "s_last": s_last}
+
+
+def conv_bwd(x, w, bias, dy, s0=None):
+    """Adjoint of conv_fwd.  Returns dict(dx, dw, dbias, ds0), all f64; dw and dbias
+    are summed over batch and time; ds0 is the gradient of the initial ring."""
+    bt, L, d, k = _conv_dims(x, w)
+    args = [_f64(a) for a in (x, w, bias, s0, dy)]
+    out = {"dx": np.empty((bt, L, d)), "dw": np.empty((d, k)), "dbias": np.empty(d),
+           "ds0": np.empty((bt, d, k - 1))}
+    rc = _load().oracle_conv_bwd(bt, L, d, k, *[_ptr(a) for a in args],
+                                 *[_ptr(out[n]) for n in ("dx", "dw", "dbias", "ds0")])
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv_bwd failed: {rc}")
+    return out
+
+
+def conv_step(ring, x, w, bias):
+    """One token of conv_fwd.  ring: f64 [batch, d_inner, d_conv-1], updated in
+    place (drops the oldest input, appends x); x: [batch, d_inner].  Returns y."""
+    if not (isinstance(ring, np.ndarray) and ring.dtype == np.float64 and ring.flags.c_contiguous):
+        raise ValueError("ring must be a C-contiguous float64 array (updated in place)")
+    w = _f64(w)
+    bt, d = np.asarray(x).shape
+    k = w.shape[1]
+    y = np.empty((bt, d))
+    rc = _load().oracle_conv_step(bt, d, k, _ptr(ring), _ptr(_f64(x)), _ptr(w), _ptr(_f64(bias)), _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv_step failed: {rc}")
     return y
