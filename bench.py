@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--cpu-sample-channels", type=int, default=0,
                     help="channels the oracle baseline runs on (0 = all)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--op", choices=("scan", "conv1d"), default="scan",
+                    help="scan: the selective scan fwd+bwd (default); conv1d: the causal depthwise "
+                         "conv1d + SiLU fwd+bwd in front of it, on the same batch/seqlen/d_inner")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to calibrate "
                          "profiler FETCH_SIZE / WRITE_SIZE counters")
@@ -112,12 +115,105 @@ def cpu_baseline(inp, cfg, rows, channels):
                       f"the same workload, fwd+bwd in f64 ({elems} elements, {sec:.1f} s)"}
 
 
+def conv_bench(args):
+    """Causal depthwise conv1d + SiLU, forward + backward, on the conv workload."""
+    import numpy as np
+    import torch
+
+    import selective_state_space_04_amd as ssm
+    import workloads as W
+
+    name = "conv_mamba2p8b_bf16"
+    cfg = W.CONV_CONFIGS[name]
+    dev = torch.device("cuda:0")
+    io = torch.bfloat16 if cfg["io"] == "bf16" else torch.float32
+    esz = 2 if io == torch.bfloat16 else 4
+    print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
+    inp = W.make_conv_config(name)
+    x = torch.from_numpy(inp["x"]).to(dev).to(io)
+    dy = torch.from_numpy(inp["dy"]).to(dev).to(io)
+    w = torch.from_numpy(inp["w"]).to(dev)
+    bias = torch.from_numpy(inp["bias"]).to(dev)
+    bsz, L, D = x.shape
+    K = w.shape[1]
+    y = torch.empty_like(x)
+    grads = {"dx": torch.empty_like(x), "dw": torch.empty_like(w), "dbias": torch.empty_like(bias),
+             "dring0": None}
+
+    def step(timer=None):
+        ssm.ssm_conv1d_fwd(x, w, bias, y=y, timing=timer)
+        ssm.ssm_conv1d_bwd(x, w, bias, dy, out=grads, timing=timer)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [ssm.LaunchTimer() for _ in range(args.steps)]
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(timers[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per_kernel = {}
+    for tm in timers:
+        for kname, kms in tm.results():
+            per_kernel.setdefault(kname, []).append(kms)
+        tm.close()
+    kavg = {k: float(np.mean(v)) for k, v in per_kernel.items()}
+    btd = bsz * L * D
+    # compulsory bytes: forward reads x, writes y; backward reads x, dy, writes dx
+    kbytes = {"k_conv_fwd": btd * esz * 2 + 4 * D * (K + 1),
+              "k_conv_bwd": btd * esz * 3 + 4 * D * (K + 1)}
+    dominant = max(kbytes, key=lambda k: kavg.get(k, 0.0))
+    gbps = kbytes[dominant] / (kavg[dominant] * 1e-3) / 1e9
+    line = {
+        "metric": "causal depthwise conv1d+SiLU fwd+bwd elements(B\u00b7L\u00b7D)/s and achieved HBM GB/s",
+        "value": btd / (ms * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: batch={bsz} seqlen={L} d_inner={D} d_conv={K}, {cfg['io']} "
+                               f"activations, f32 weights and arithmetic, fwd+bwd",
+                   "batch": bsz, "seqlen": L, "d_inner": D, "d_conv": K, "io_dtype": cfg["io"]},
+        "achieved_hbm_GBps": round(sum(kbytes.values()) / (ms * 1e-3) / 1e9, 1),
+        "kernels_ms": {k: round(v, 4) for k, v in sorted(kavg.items())},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dominant,
+                     "kernel_ms": round(kavg[dominant], 4), "algorithmic_bytes_per_launch": kbytes[dominant]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = min(args.cpu_sample_rows, bsz)
+        sub = {k: np.ascontiguousarray(inp[k][:rows]).astype(np.float64) for k in ("x", "dy")}
+        t0 = time.perf_counter()
+        oracle.conv_fwd(sub["x"], inp["w"], inp["bias"])
+        oracle.conv_bwd(sub["x"], inp["w"], inp["bias"], sub["dy"])
+        sec = time.perf_counter() - t0
+        el = rows * L * D
+        line["cpu_baseline"] = {"value": el / sec, "unit": "elements/s", "cores": oracle.num_threads(),
+                                "kind": "oracle",
+                                "sample": f"batch rows 0..{rows - 1}, all {L} tokens and {D} channels of the "
+                                          f"same workload, fwd+bwd in f64 ({el} elements, {sec:.1f} s)"}
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(s + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the scan is measured on a "
               f"single MI355X and multi-GPU sharding is design-only.", file=sys.stderr)
         sys.exit(2)
+    if args.op == "conv1d":
+        conv_bench(args)
+        return
 
     import numpy as np
     import torch

@@ -69,7 +69,7 @@ typedef enum {
     SSM_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     SSM_E_WORKSPACE = 5,   /* workspace smaller than the query function returns */
     SSM_E_LAUNCH = 6,      /* a kernel launch failed (hipGetLastError) */
-    SSM_E_UNSUPPORTED = 7  /* valid but unsupported (d_state != 16, batch > 65535) */
+    SSM_E_UNSUPPORTED = 7  /* valid but unsupported (d_state != 16, d_conv > 4, batch > 65535) */
 } ssm_status;
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -108,7 +108,12 @@ enum {
     SSM_K_BWD_REDUCE_BC = 7, /* fixed-order sum of dB/dC partials over channel blocks */
     SSM_K_BWD_REDUCE_P = 8,  /* fixed-order sum of dA_log/dD/ddt_bias partials */
     SSM_K_STEP = 9,          /* single-token state update */
-    SSM_K_FILL = 10          /* small fills for seqlen == 0 */
+    SSM_K_FILL = 10,         /* small fills for seqlen == 0 */
+    SSM_K_CONV_FWD = 11,     /* causal depthwise conv1d + SiLU (ssm_conv1d.h) */
+    SSM_K_CONV_BWD = 12,     /* its adjoint: dx, ring gradient, dw/dbias partials */
+    SSM_K_CONV_BWD_REDUCE = 13, /* fixed-order sum of dw/dbias partials */
+    SSM_K_CONV_STEP = 14,    /* one token through the conv ring */
+    SSM_K_CONV_RING = 15     /* ring copies/fills when seqlen == 0 */
 };
 
 /* Name of a kernel id (for matching profiler output); "?" if unknown. */

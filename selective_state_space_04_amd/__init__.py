@@ -1,9 +1,9 @@
 """MI355X-native Mamba S6 selective scan.
 
-Thin Python binding of ``libssmscan.so`` (built from ``csrc/ssm_scan.hip``): it
-checks tensors, allocates outputs/workspace through torch's caching allocator
-and passes raw device pointers and the current HIP stream to the C ABI declared
-in ``include/ssm_scan.h``.  Every step of the scan runs in the library's HIP
+Thin Python binding of ``libssmscan.so`` (built from ``csrc/ssm_scan.hip`` and
+``csrc/ssm_conv1d.hip``): it checks tensors, allocates outputs/workspace through
+torch's caching allocator and passes raw device pointers and the current HIP
+stream to the C ABI declared in ``include/ssm_scan.h`` and ``include/ssm_conv1d.h``.  Every step of the scan runs in the library's HIP
 kernels; there is no other code path.  Importing fails loudly when the library
 has not been built (``__graft_entry__.build()``).
 
@@ -12,6 +12,8 @@ commits introducing the real S6 forward, its hand-written VJP and
 MambaRecurrence::step):
     delta = softplus(dt + dt_bias), A = -exp(A_log)
     h_t   = exp(delta*A) h_{t-1} + delta B_t x_t,   y_t = (C_t.h_t + D x_t) silu(z_t)
+and, in front of it, the causal depthwise conv1d + SiLU with its conv ring
+(same page: the real-S6-forward commit's in_proj -> conv1d -> SiLU -> x_proj).
 """
 import ctypes
 import os
@@ -30,6 +32,12 @@ TIMING_MAX = 16
 class SsmDims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
                 ("d_inner", ctypes.c_int64), ("d_state", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32)]
+
+
+class ConvDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("d_inner", ctypes.c_int64), ("d_conv", ctypes.c_int64),
                 ("io_dtype", ctypes.c_int32)]
 
 
@@ -66,6 +74,15 @@ def _load_library():
     lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_scan_step.argtypes = [I64, I64, I64, I32] + [P] * 10 + [P, TP]
     lib.ssm_scan_step.restype = ctypes.c_int
+    CP = ctypes.POINTER(ConvDims)
+    lib.ssm_conv1d_bwd_workspace_bytes.argtypes = [CP]
+    lib.ssm_conv1d_bwd_workspace_bytes.restype = SZ
+    lib.ssm_conv1d_fwd.argtypes = [CP] + [P] * 6 + [P, TP]
+    lib.ssm_conv1d_fwd.restype = ctypes.c_int
+    lib.ssm_conv1d_bwd.argtypes = [CP] + [P] * 9 + [P, SZ, P, TP]
+    lib.ssm_conv1d_bwd.restype = ctypes.c_int
+    lib.ssm_conv1d_step.argtypes = [I64, I64, I64, I32] + [P] * 5 + [P, TP]
+    lib.ssm_conv1d_step.restype = ctypes.c_int
     return lib
 
 
@@ -248,6 +265,96 @@ def ssm_scan_step(h, x, dt, B, C, z, A_log, D, dt_bias, *, y=None, stream=None, 
     return y
 
 
+def conv_dims(batch, seqlen, d_inner, d_conv, io_dtype=torch.float32):
+    return ConvDims(int(batch), int(seqlen), int(d_inner), int(d_conv), _io_code(io_dtype))
+
+
+def conv1d_bwd_workspace_bytes(batch, seqlen, d_inner, d_conv, io_dtype=torch.float32):
+    return int(_lib.ssm_conv1d_bwd_workspace_bytes(ctypes.byref(conv_dims(batch, seqlen, d_inner, d_conv,
+                                                                          io_dtype))))
+
+
+def _ring(t, name, bsz, din, k, dev, required=False):
+    if k == 1:
+        return None  # width 1: the ring is empty and ignored
+    _check(t, name, (bsz, din, k - 1), torch.float32, dev, required=required)
+    return t
+
+
+def ssm_conv1d_fwd(x, w, bias=None, ring0=None, *, return_ring=False, y=None, stream=None, timing=None):
+    """Causal depthwise conv1d + SiLU.  x [batch, L, d_inner] (float32 or bfloat16);
+    w [d_inner, d_conv] float32 (PyTorch's [d_inner, 1, d_conv] squeezed); bias
+    [d_inner] float32 or None; ring0 [batch, d_inner, d_conv-1] float32: the inputs
+    before the sequence (None = zeros).  Returns (y, ring_last or None)."""
+    dev = x.device
+    bsz, L, din = x.shape
+    io = x.dtype
+    k = w.shape[1] if w.dim() == 2 else -1
+    _check(x, "x", (bsz, L, din), io, dev)
+    _check(w, "w", (din, k), torch.float32, dev)
+    _check(bias, "bias", (din,), torch.float32, dev, required=False)
+    ring0 = _ring(ring0, "ring0", bsz, din, k, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (bsz, L, din), io, dev)
+    ring_last = torch.empty(bsz, din, k - 1, dtype=torch.float32, device=dev) if return_ring and k > 1 else None
+    dm = conv_dims(bsz, L, din, k, io)
+    rc = _lib.ssm_conv1d_fwd(ctypes.byref(dm), _ptr(x), _ptr(w), _ptr(bias), _ptr(ring0), _ptr(y),
+                             _ptr(ring_last), _stream(dev, stream), _timing_ptr(timing))
+    _raise("ssm_conv1d_fwd", rc)
+    return y, ring_last
+
+
+def ssm_conv1d_bwd(x, w, bias, dy, ring0=None, *, want_dring0=False, stream=None, timing=None, out=None):
+    """Backward of ssm_conv1d_fwd for the loss sum(dy * y).  Returns a dict with dx
+    (io dtype), dw [d_inner, d_conv], dbias [d_inner] and dring0 (float32; None
+    unless want_dring0)."""
+    dev = x.device
+    bsz, L, din = x.shape
+    io = x.dtype
+    k = w.shape[1] if w.dim() == 2 else -1
+    _check(x, "x", (bsz, L, din), io, dev)
+    _check(dy, "dy", (bsz, L, din), io, dev)
+    _check(w, "w", (din, k), torch.float32, dev)
+    _check(bias, "bias", (din,), torch.float32, dev, required=False)
+    ring0 = _ring(ring0, "ring0", bsz, din, k, dev)
+    g = out if out is not None else {}
+    g.setdefault("dx", torch.empty_like(x))
+    g.setdefault("dw", torch.empty_like(w))
+    g.setdefault("dbias", torch.empty(din, dtype=torch.float32, device=dev))
+    g.setdefault("dring0", torch.empty(bsz, din, k - 1, dtype=torch.float32, device=dev)
+                 if want_dring0 and k > 1 else None)
+    dm = conv_dims(bsz, L, din, k, io)
+    nws = _lib.ssm_conv1d_bwd_workspace_bytes(ctypes.byref(dm))
+    ws = _workspace(nws, dev)
+    rc = _lib.ssm_conv1d_bwd(ctypes.byref(dm), _ptr(x), _ptr(w), _ptr(bias), _ptr(ring0), _ptr(dy),
+                             _ptr(g["dx"]), _ptr(g["dw"]), _ptr(g["dbias"]), _ptr(g["dring0"]), _ptr(ws), nws,
+                             _stream(dev, stream), _timing_ptr(timing))
+    _raise("ssm_conv1d_bwd", rc)
+    return g
+
+
+def ssm_conv1d_step(ring, x, w, bias=None, *, y=None, stream=None, timing=None):
+    """One token through the conv ring: ring [batch, d_inner, d_conv-1] float32 is
+    updated in place (ignored for d_conv 1); x [batch, d_inner] io dtype.
+    Returns y [batch, d_inner]."""
+    dev = x.device
+    bsz, din = x.shape
+    io = x.dtype
+    k = w.shape[1] if w.dim() == 2 else -1
+    _check(x, "x", (bsz, din), io, dev)
+    _check(w, "w", (din, k), torch.float32, dev)
+    _check(bias, "bias", (din,), torch.float32, dev, required=False)
+    ring = _ring(ring, "ring", bsz, din, k, dev, required=True)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (bsz, din), io, dev)
+    rc = _lib.ssm_conv1d_step(bsz, din, k, _io_code(io), _ptr(ring), _ptr(x), _ptr(w), _ptr(bias), _ptr(y),
+                              _stream(dev, stream), _timing_ptr(timing))
+    _raise("ssm_conv1d_step", rc)
+    return y
+
+
 class LaunchTimer:
     """Per-kernel timing through the ABI's optional launch log: HIP events recorded
     by the library around each of its launches, on the launch stream."""
@@ -298,4 +405,5 @@ class LaunchTimer:
 
 __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_scan_step", "ckpt_bytes", "fwd_workspace_bytes",
            "bwd_workspace_bytes", "LaunchTimer", "SsmError", "library", "status_str", "kernel_name",
-           "SsmDims", "SsmTiming"]
+           "SsmDims", "SsmTiming", "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_conv1d_step",
+           "conv1d_bwd_workspace_bytes", "ConvDims"]

@@ -1,10 +1,11 @@
-"""Compiles libssmscan.so (HIP, gfx950 only) in-tree with hipcc."""
+"""Compiles libssmscan.so (HIP, gfx950 only: the selective scan and the conv1d
+in front of it) in-tree with hipcc."""
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "ssm_scan.hip")
+SRCS = [os.path.join(HERE, "csrc", "ssm_scan.hip"), os.path.join(HERE, "csrc", "ssm_conv1d.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libssmscan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -20,7 +21,7 @@ FLAGS = [
 
 def build(verbose=False, extra=()):
     tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,557 @@
+// ssm_conv1d.hip -- causal depthwise conv1d + SiLU in front of the selective scan,
+// for MI355X (gfx950, CDNA4, wave64).
+//
+// Operation (rustytorch commit log, page "crates/training/rtx-transformers/tests":
+// the real-S6-forward commit runs a causal depthwise conv1d then SiLU before
+// x_proj; the VJP commit returns conv1d_weight / conv1d_bias gradients;
+// MambaRecurrence::step carries a conv ring), read as PyTorch's
+// Conv1d(groups=d_inner, padding=K-1) truncated to the first L outputs:
+//   pre[b,t,d] = bias[d] + sum_k w[d,k] * v[b, t-(K-1)+k, d],   y = silu(pre)
+// with v = x at t >= 0 and the caller's ring of the K-1 previous inputs before.
+//
+// Mapping to the hardware.  The operation is a K-tap stencil along time with no
+// reuse across channels: HBM-bound, a few flops per byte.
+//   * A lane owns VEC = 4 consecutive channels (8 or 16 contiguous bytes per
+//     token), so a wave reads 64 * VEC channels of one token as one coalesced
+//     512 B / 1 KB row; rows whose d_inner is not a multiple of 4 use VEC = 1.
+//   * A wave streams a run of TT = 64 tokens with a sliding window of the last
+//     K inputs in registers, PF = 8 tokens of loads in flight; the 4 waves of a
+//     workgroup take 4 consecutive runs, so the K-1 token halo a run re-reads
+//     was just read by its neighbour (L2 hit).
+//   * Backward: g = dy * silu'(pre) needs the forward's pre, recomputed from the
+//     window; dx[t] = sum_k w[k] g[t+K-1-k] needs g K-1 tokens ahead, so a run
+//     computes g over TT + K - 1 tokens.  dw/dbias are summed per lane over the
+//     run, across the 4 waves through LDS, and across workgroups by a
+//     fixed-order kernel: deterministic, no atomics.
+//   * The step shares the forward's per-token arithmetic (bias first, taps in
+//     increasing k, explicit FMAs), so stepping reproduces the forward exactly.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+#include "ssm_common.h"
+#include "ssm_conv1d.h"
+
+namespace {
+
+using ssm::bf16_t;
+using ssm::from_f;
+using ssm::misaligned;
+using ssm::sigmoid_f;
+using ssm::to_f;
+
+constexpr int WG = 256;  // 64 lanes (channel groups) x 4 waves (token runs)
+constexpr int NWAVE = WG / 64;
+constexpr int TT = 64;   // tokens per wave
+constexpr int PF = 8;    // tokens fetched ahead
+constexpr int KMAX = 4;
+
+// ---------------------------------------------------------------- VEC channels
+template <typename T, int VEC> struct Raw;
+template <> struct Raw<float, 4> { typedef float4 type; };
+template <> struct Raw<bf16_t, 4> { typedef uint2 type; };
+template <> struct Raw<float, 1> { typedef float type; };
+template <> struct Raw<bf16_t, 1> { typedef bf16_t type; };
+
+template <typename T, int VEC>
+__device__ __forceinline__ typename Raw<T, VEC>::type ld(const T* p) {
+    return *reinterpret_cast<const typename Raw<T, VEC>::type*>(p);
+}
+
+__device__ __forceinline__ void unpack(float4 r, float v[4]) {
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+}
+__device__ __forceinline__ void unpack(uint2 r, float v[4]) {
+    v[0] = __uint_as_float(r.x << 16);
+    v[1] = __uint_as_float(r.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.y << 16);
+    v[3] = __uint_as_float(r.y & 0xffff0000u);
+}
+__device__ __forceinline__ void unpack(float r, float v[1]) { v[0] = r; }
+__device__ __forceinline__ void unpack(bf16_t r, float v[1]) { v[0] = to_f(r); }
+
+template <typename T, int VEC> __device__ __forceinline__ void st(T* p, const float v[VEC]);
+template <> __device__ __forceinline__ void st<float, 4>(float* p, const float v[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void st<bf16_t, 4>(bf16_t* p, const float v[4]) {
+    uint2 u;
+    u.x = (uint32_t)from_f<bf16_t>(v[0]) | ((uint32_t)from_f<bf16_t>(v[1]) << 16);
+    u.y = (uint32_t)from_f<bf16_t>(v[2]) | ((uint32_t)from_f<bf16_t>(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = u;
+}
+template <> __device__ __forceinline__ void st<float, 1>(float* p, const float v[1]) { p[0] = v[0]; }
+template <> __device__ __forceinline__ void st<bf16_t, 1>(bf16_t* p, const float v[1]) {
+    p[0] = from_f<bf16_t>(v[0]);
+}
+
+// pre-activation of one channel: bias first, then the taps in increasing k.
+template <int K>
+__device__ __forceinline__ float conv_pre(float bias, const float w[K], const float v[K]) {
+    float acc = bias;
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[k], v[k], acc);
+    return acc;
+}
+
+// Per-lane setup shared by the forward and backward: weights, bias, and the K-1
+// inputs before token t0 (from x, or from the ring / zero before the sequence).
+template <typename T, int K, int VEC>
+__device__ __forceinline__ void conv_prologue(const T* __restrict__ x, const float* __restrict__ w,
+                                              const float* __restrict__ bias,
+                                              const float* __restrict__ ring0, int b, int c0, int t0,
+                                              int L, int D, float wk[VEC][K], float bs[VEC],
+                                              float win[K][VEC]) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) wk[v][k] = w[(int64_t)(c0 + v) * K + k];
+        bs[v] = bias ? bias[c0 + v] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+        const int tau = t0 - (K - 1) + j;
+        if (tau >= 0) {
+            unpack(ld<T, VEC>(x + ((int64_t)b * L + tau) * D + c0), win[j]);
+        } else {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v)
+                win[j][v] = ring0 ? ring0[((int64_t)b * D + c0 + v) * (K - 1) + (tau + K - 1)] : 0.0f;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ forward
+template <typename T, int K, int VEC>
+__global__ __launch_bounds__(WG) void k_conv_fwd(const T* __restrict__ x, const float* __restrict__ w,
+                                                 const float* __restrict__ bias,
+                                                 const float* __restrict__ ring0, T* __restrict__ y,
+                                                 float* __restrict__ ring_last, int L, int D) {
+    typedef typename Raw<T, VEC>::type R;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c0 = (blockIdx.x * 64 + lane) * VEC;
+    const int b = blockIdx.z;
+    const int t0 = (blockIdx.y * NWAVE + wave) * TT;
+    if (c0 >= D || t0 >= L) return;  // no barrier in this kernel
+    const int t1 = min(t0 + TT, L);
+    float wk[VEC][K], bs[VEC], win[K][VEC];
+    conv_prologue<T, K, VEC>(x, w, bias, ring0, b, c0, t0, L, D, wk, bs, win);
+    const T* xp = x + (int64_t)b * L * D + c0;
+    T* yp = y + (int64_t)b * L * D + c0;
+    R q[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (t0 + p < t1) q[p] = ld<T, VEC>(xp + (int64_t)(t0 + p) * D);
+    for (int u = t0; u < t1; u += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int uu = u + p;
+            if (uu < t1) {
+                unpack(q[p], win[K - 1]);
+                if (uu + PF < t1) q[p] = ld<T, VEC>(xp + (int64_t)(uu + PF) * D);
+                float out[VEC];
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    float tap[K];
+#pragma unroll
+                    for (int k = 0; k < K; ++k) tap[k] = win[k][v];
+                    const float pre = conv_pre<K>(bs[v], wk[v], tap);
+                    out[v] = pre * sigmoid_f(pre);
+                }
+                st<T, VEC>(yp + (int64_t)uu * D, out);
+#pragma unroll
+                for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) win[j][v] = win[j + 1][v];
+            }
+        }
+    }
+    // the last K-1 inputs (oldest first) continue the stream
+    if (t1 == L && ring_last) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+#pragma unroll
+            for (int j = 0; j < K - 1; ++j)
+                ring_last[((int64_t)b * D + c0 + v) * (K - 1) + j] = win[j][v];
+    }
+}
+
+// ------------------------------------------------------------------ backward
+// part: [Bt * gridDim.y, D, K+1] per-workgroup sums (dw taps, then dbias).
+template <typename T, int K, int VEC>
+__global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const float* __restrict__ w,
+                                                 const float* __restrict__ bias,
+                                                 const float* __restrict__ ring0,
+                                                 const T* __restrict__ dy, T* __restrict__ dx,
+                                                 float* __restrict__ dring0, float* __restrict__ part,
+                                                 int L, int D) {
+    typedef typename Raw<T, VEC>::type R;
+    constexpr int NP = (K + 1) * VEC;
+    __shared__ float red[NWAVE][NP][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c0 = (blockIdx.x * 64 + lane) * VEC;
+    const int b = blockIdx.z;
+    const int t0 = (blockIdx.y * NWAVE + wave) * TT;
+    float dwa[K][VEC], dba[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        dba[v] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) dwa[k][v] = 0.0f;
+    }
+    if (c0 < D && t0 < L) {
+        const int t1 = min(t0 + TT, L);
+        const int uend = t1 + K - 1;  // g is needed K-1 tokens past the run
+        const int lend = min(uend, L);  // tokens that exist
+        float wk[VEC][K], bs[VEC], win[K][VEC], gw[K][VEC], dr[KMAX][VEC];
+        conv_prologue<T, K, VEC>(x, w, bias, ring0, b, c0, t0, L, D, wk, bs, win);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) gw[k][v] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) dr[j][v] = 0.0f;
+        }
+        const int64_t base = (int64_t)b * L * D + c0;
+        const T* xp = x + base;
+        const T* gp = dy + base;
+        T* dxp = dx + base;
+        R qx[PF], qg[PF];
+#pragma unroll
+        for (int p = 0; p < PF; ++p)
+            if (t0 + p < lend) {
+                qx[p] = ld<T, VEC>(xp + (int64_t)(t0 + p) * D);
+                qg[p] = ld<T, VEC>(gp + (int64_t)(t0 + p) * D);
+            }
+        for (int u = t0; u < uend; u += PF) {
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                const int uu = u + p;
+                if (uu < uend) {
+                    float g[VEC];
+                    if (uu < L) {
+                        float dyv[VEC];
+                        unpack(qx[p], win[K - 1]);
+                        unpack(qg[p], dyv);
+                        if (uu + PF < lend) {
+                            qx[p] = ld<T, VEC>(xp + (int64_t)(uu + PF) * D);
+                            qg[p] = ld<T, VEC>(gp + (int64_t)(uu + PF) * D);
+                        }
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) {
+                            float tap[K];
+#pragma unroll
+                            for (int k = 0; k < K; ++k) tap[k] = win[k][v];
+                            const float pre = conv_pre<K>(bs[v], wk[v], tap);
+                            const float s = sigmoid_f(pre);
+                            // d silu / d pre = s * (1 + pre * (1 - s))
+                            g[v] = dyv[v] * (s * __builtin_fmaf(pre, 1.0f - s, 1.0f));
+                        }
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) g[v] = 0.0f;
+                    }
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) gw[K - 1][v] = g[v];
+                    if (uu < t1) {  // this run's own tokens
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) {
+                            dba[v] += g[v];
+#pragma unroll
+                            for (int k = 0; k < K; ++k) dwa[k][v] = __builtin_fmaf(g[v], win[k][v], dwa[k][v]);
+                        }
+                    }
+                    // taps before the sequence: input time j-(K-1) of the ring
+                    if (uu < K - 1) {
+#pragma unroll
+                        for (int j = 0; j < K - 1; ++j)
+                            if (j >= uu)
+#pragma unroll
+                                for (int v = 0; v < VEC; ++v)
+                                    dr[j][v] = __builtin_fmaf(wk[v][j - uu], g[v], dr[j][v]);
+                    }
+                    const int tau = uu - (K - 1);
+                    if (tau >= t0) {
+                        float o[VEC];
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) {
+                            float acc = 0.0f;
+#pragma unroll
+                            for (int k = 0; k < K; ++k) acc = __builtin_fmaf(wk[v][k], gw[K - 1 - k][v], acc);
+                            o[v] = acc;
+                        }
+                        st<T, VEC>(dxp + (int64_t)tau * D, o);
+                    }
+#pragma unroll
+                    for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) {
+                            win[j][v] = win[j + 1][v];
+                            gw[j][v] = gw[j + 1][v];
+                        }
+                }
+            }
+        }
+        if (t0 == 0 && dring0) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v)
+#pragma unroll
+                for (int j = 0; j < K - 1; ++j)
+                    dring0[((int64_t)b * D + c0 + v) * (K - 1) + j] = dr[j][v];
+        }
+    }
+    // dw / dbias: this lane's sums over its run, then over the 4 runs in order
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) red[wave][k * VEC + v][lane] = dwa[k][v];
+        red[wave][K * VEC + v][lane] = dba[v];
+    }
+    __syncthreads();
+    for (int e = wave; e < NP; e += NWAVE) {
+        const float s = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
+        const int k = e / VEC, v = e % VEC;
+        if (c0 + v < D)
+            part[(((int64_t)b * gridDim.y + blockIdx.y) * D + c0 + v) * (K + 1) + k] = s;
+    }
+}
+
+// dw[d,k] / dbias[d] = sum over tiles (fixed order) of the partials.
+__global__ __launch_bounds__(WG) void k_conv_bwd_reduce(const float* __restrict__ part,
+                                                        float* __restrict__ dw,
+                                                        float* __restrict__ dbias, int64_t ntiles,
+                                                        int D, int K) {
+    const int64_t idx = (int64_t)blockIdx.x * WG + threadIdx.x;
+    const int64_t per = (int64_t)D * (K + 1);
+    if (idx >= per) return;
+    float s = 0.0f;
+    for (int64_t t = 0; t < ntiles; ++t) s += part[t * per + idx];
+    const int d = (int)(idx / (K + 1)), k = (int)(idx % (K + 1));
+    if (k < K) dw[(int64_t)d * K + k] = s;
+    else dbias[d] = s;
+}
+
+// ------------------------------------------------------------------ step
+template <typename T, int K>
+__global__ __launch_bounds__(WG) void k_conv_step(float* __restrict__ ring, const T* __restrict__ x,
+                                                  const float* __restrict__ w,
+                                                  const float* __restrict__ bias, T* __restrict__ y,
+                                                  int64_t n, int D) {
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (i >= n) return;
+    const int d = (int)(i % D);
+    const float xv = to_f(x[i]);
+    float* r = ring + i * (K - 1);
+    float wk[K], tap[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = w[(int64_t)d * K + k];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) tap[k] = r[k];
+    tap[K - 1] = xv;
+    const float pre = conv_pre<K>(bias ? bias[d] : 0.0f, wk, tap);
+    y[i] = from_f<T>(pre * sigmoid_f(pre));
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) r[j] = tap[j + 1];
+}
+
+// dst[i] = src ? src[i] : 0
+__global__ __launch_bounds__(WG) void k_conv_fill(float* __restrict__ dst,
+                                                  const float* __restrict__ src, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+// ------------------------------------------------------------------ host side
+struct ConvPlan {
+    int64_t Bt, L, D, K;
+    int io;
+    int vec;       // channels per lane (4, or 1 when d_inner % 4 != 0)
+    int64_t gx, gy;
+};
+
+ssm_status check_conv(const ssm_conv_dims* d) {
+    if (!d) return SSM_E_NULLPTR;
+    if (d->batch <= 0 || d->seqlen < 0 || d->d_inner <= 0 || d->d_conv <= 0) return SSM_E_SHAPE;
+    if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_E_DTYPE;
+    if (d->d_conv > KMAX || d->batch > 65535 || d->d_inner > INT_MAX / 4 ||
+        d->seqlen > (int64_t)65535 * NWAVE * TT)
+        return SSM_E_UNSUPPORTED;
+    return SSM_OK;
+}
+
+ConvPlan conv_plan(const ssm_conv_dims* d) {
+    ConvPlan p;
+    p.Bt = d->batch;
+    p.L = d->seqlen;
+    p.D = d->d_inner;
+    p.K = d->d_conv;
+    p.io = d->io_dtype;
+    p.vec = p.D % 4 == 0 ? 4 : 1;
+    p.gx = (p.D / p.vec + 63) / 64;
+    p.gy = (p.L + NWAVE * TT - 1) / (NWAVE * TT);
+    return p;
+}
+
+size_t conv_ws_bytes(const ConvPlan& p) {
+    return sizeof(float) * (size_t)(p.Bt * p.gy * p.D * (p.K + 1));
+}
+
+struct Launcher {
+    ssm::Launcher l;
+    template <typename Kern, typename... Args>
+    ssm_status operator()(int kid, Kern kern, dim3 grid, Args... args) {
+        return l(kid, kern, grid, dim3(WG), args...);
+    }
+};
+
+template <typename T, int K, int VEC>
+ssm_status run_fwd(const ConvPlan& p, const void* x, const float* w, const float* bias,
+                   const float* ring0, void* y, float* ring_last, Launcher& launch) {
+    return launch(SSM_K_CONV_FWD, k_conv_fwd<T, K, VEC>, dim3((unsigned)p.gx, (unsigned)p.gy, (unsigned)p.Bt),
+                  (const T*)x, w, bias, ring0, (T*)y, ring_last, (int)p.L, (int)p.D);
+}
+
+template <typename T, int K, int VEC>
+ssm_status run_bwd(const ConvPlan& p, const void* x, const float* w, const float* bias,
+                   const float* ring0, const void* dy, void* dx, float* dw, float* dbias,
+                   float* dring0, float* part, Launcher& launch) {
+    SSM_TRY(launch(SSM_K_CONV_BWD, k_conv_bwd<T, K, VEC>,
+                   dim3((unsigned)p.gx, (unsigned)p.gy, (unsigned)p.Bt), (const T*)x, w, bias, ring0,
+                   (const T*)dy, (T*)dx, dring0, part, (int)p.L, (int)p.D));
+    const int64_t per = p.D * (p.K + 1);
+    return launch(SSM_K_CONV_BWD_REDUCE, k_conv_bwd_reduce, dim3((unsigned)((per + WG - 1) / WG)),
+                  (const float*)part, dw, dbias, p.Bt * p.gy, (int)p.D, (int)p.K);
+}
+
+// The forward / backward launch for one (io dtype, K, VEC) instantiation.
+struct FwdCall {
+    const ConvPlan& p; const void* x; const float* w; const float* bias; const float* ring0;
+    void* y; float* ring_last; Launcher& launch;
+    template <typename T, int K, int VEC> ssm_status run() {
+        return run_fwd<T, K, VEC>(p, x, w, bias, ring0, y, ring_last, launch);
+    }
+};
+struct BwdCall {
+    const ConvPlan& p; const void* x; const float* w; const float* bias; const float* ring0;
+    const void* dy; void* dx; float* dw; float* dbias; float* dring0; float* part; Launcher& launch;
+    template <typename T, int K, int VEC> ssm_status run() {
+        return run_bwd<T, K, VEC>(p, x, w, bias, ring0, dy, dx, dw, dbias, dring0, part, launch);
+    }
+};
+
+// Instantiation over (io dtype, K, VEC) for the forward and backward.
+template <int K, int VEC, typename F>
+ssm_status by_dtype(int io, F&& f) {
+    return io == SSM_F32 ? f.template run<float, K, VEC>() : f.template run<bf16_t, K, VEC>();
+}
+
+template <typename F>
+ssm_status dispatch(const ConvPlan& p, F&& f) {
+    const bool v4 = p.vec == 4;
+    switch (p.K) {
+        case 1: return v4 ? by_dtype<1, 4>(p.io, f) : by_dtype<1, 1>(p.io, f);
+        case 2: return v4 ? by_dtype<2, 4>(p.io, f) : by_dtype<2, 1>(p.io, f);
+        case 3: return v4 ? by_dtype<3, 4>(p.io, f) : by_dtype<3, 1>(p.io, f);
+        default: return v4 ? by_dtype<4, 4>(p.io, f) : by_dtype<4, 1>(p.io, f);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_conv1d_bwd_workspace_bytes(const ssm_conv_dims* dims) {
+    if (check_conv(dims) != SSM_OK || dims->seqlen == 0) return 0;
+    return conv_ws_bytes(conv_plan(dims));
+}
+
+ssm_status ssm_conv1d_fwd(const ssm_conv_dims* dims, const void* x, const float* w,
+                          const float* bias, const float* ring0, void* y, float* ring_last,
+                          hipStream_t stream, ssm_timing* timing) {
+    SSM_TRY(check_conv(dims));
+    const ConvPlan p = conv_plan(dims);
+    if (!w) return SSM_E_NULLPTR;
+    if (p.L > 0 && (!x || !y)) return SSM_E_NULLPTR;
+    if (p.K == 1) ring0 = ring_last = nullptr;
+    if (ring_last && ring_last == ring0) return SSM_E_UNSUPPORTED;
+    const void* ptrs[] = {x, w, bias, ring0, y, ring_last};
+    for (const void* q : ptrs)
+        if (q && misaligned(q)) return SSM_E_ALIGN;
+    (void)hipGetLastError();
+    Launcher launch{{stream, timing}};
+    if (p.L == 0) {
+        if (!ring_last) return SSM_OK;
+        const int64_t n = p.Bt * p.D * (p.K - 1);
+        return launch(SSM_K_CONV_RING, k_conv_fill, dim3((unsigned)((n + WG - 1) / WG)), ring_last, ring0, n);
+    }
+    FwdCall f{p, x, w, bias, ring0, y, ring_last, launch};
+    return dispatch(p, f);
+}
+
+ssm_status ssm_conv1d_bwd(const ssm_conv_dims* dims, const void* x, const float* w,
+                          const float* bias, const float* ring0, const void* dy, void* dx,
+                          float* dw, float* dbias, float* dring0, void* ws, size_t ws_bytes,
+                          hipStream_t stream, ssm_timing* timing) {
+    SSM_TRY(check_conv(dims));
+    const ConvPlan p = conv_plan(dims);
+    if (!w || !dw || !dbias) return SSM_E_NULLPTR;
+    if (p.L > 0 && (!x || !dy || !dx)) return SSM_E_NULLPTR;
+    if (p.K == 1) ring0 = dring0 = nullptr;
+    const void* ptrs[] = {x, w, bias, ring0, dy, dx, dw, dbias, dring0, ws};
+    for (const void* q : ptrs)
+        if (q && misaligned(q)) return SSM_E_ALIGN;
+    const size_t need = p.L > 0 ? conv_ws_bytes(p) : 0;
+    if (need > 0 && (!ws || ws_bytes < need)) return SSM_E_WORKSPACE;
+    (void)hipGetLastError();
+    Launcher launch{{stream, timing}};
+    if (p.L == 0) {
+        const int64_t nw = p.D * p.K;
+        SSM_TRY(launch(SSM_K_CONV_RING, k_conv_fill, dim3((unsigned)((nw + WG - 1) / WG)), dw,
+                       (const float*)nullptr, nw));
+        SSM_TRY(launch(SSM_K_CONV_RING, k_conv_fill, dim3((unsigned)((p.D + WG - 1) / WG)), dbias,
+                       (const float*)nullptr, p.D));
+        if (dring0) {
+            const int64_t n = p.Bt * p.D * (p.K - 1);
+            SSM_TRY(launch(SSM_K_CONV_RING, k_conv_fill, dim3((unsigned)((n + WG - 1) / WG)), dring0,
+                           (const float*)nullptr, n));
+        }
+        return SSM_OK;
+    }
+    float* part = static_cast<float*>(ws);
+    BwdCall f{p, x, w, bias, ring0, dy, dx, dw, dbias, dring0, part, launch};
+    return dispatch(p, f);
+}
+
+ssm_status ssm_conv1d_step(int64_t batch, int64_t d_inner, int64_t d_conv, int32_t io_dtype,
+                           float* ring, const void* x, const float* w, const float* bias, void* y,
+                           hipStream_t stream, ssm_timing* timing) {
+    const ssm_conv_dims dims{batch, 1, d_inner, d_conv, io_dtype};
+    SSM_TRY(check_conv(&dims));
+    if (!x || !w || !y || (d_conv > 1 && !ring)) return SSM_E_NULLPTR;
+    if (d_conv == 1) ring = nullptr;
+    const void* ptrs[] = {ring, x, w, bias, y};
+    for (const void* q : ptrs)
+        if (q && misaligned(q)) return SSM_E_ALIGN;
+    (void)hipGetLastError();
+    Launcher launch{{stream, timing}};
+    const int64_t n = batch * d_inner;
+    const dim3 grid((unsigned)((n + WG - 1) / WG));
+    const int D = (int)d_inner;
+    const bool f32 = io_dtype == SSM_F32;
+    switch (d_conv) {
+        case 1:
+            return f32 ? launch(SSM_K_CONV_STEP, k_conv_step<float, 1>, grid, ring, (const float*)x, w, bias, (float*)y, n, D)
+                       : launch(SSM_K_CONV_STEP, k_conv_step<bf16_t, 1>, grid, ring, (const bf16_t*)x, w, bias, (bf16_t*)y, n, D);
+        case 2:
+            return f32 ? launch(SSM_K_CONV_STEP, k_conv_step<float, 2>, grid, ring, (const float*)x, w, bias, (float*)y, n, D)
+                       : launch(SSM_K_CONV_STEP, k_conv_step<bf16_t, 2>, grid, ring, (const bf16_t*)x, w, bias, (bf16_t*)y, n, D);
+        case 3:
+            return f32 ? launch(SSM_K_CONV_STEP, k_conv_step<float, 3>, grid, ring, (const float*)x, w, bias, (float*)y, n, D)
+                       : launch(SSM_K_CONV_STEP, k_conv_step<bf16_t, 3>, grid, ring, (const bf16_t*)x, w, bias, (bf16_t*)y, n, D);
+        default:
+            return f32 ? launch(SSM_K_CONV_STEP, k_conv_step<float, 4>, grid, ring, (const float*)x, w, bias, (float*)y, n, D)
+                       : launch(SSM_K_CONV_STEP, k_conv_step<bf16_t, 4>, grid, ring, (const bf16_t*)x, w, bias, (bf16_t*)y, n, D);
+    }
+}
+
+}  // extern "C"

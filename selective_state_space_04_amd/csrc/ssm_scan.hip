@@ -34,9 +34,16 @@
 
 #include <algorithm>
 
+#include "ssm_common.h"
 #include "ssm_scan.h"
 
 namespace {
+
+using ssm::bf16_t;
+using ssm::from_f;
+using ssm::misaligned;
+using ssm::sigmoid_f;
+using ssm::to_f;
 
 constexpr int NS = 16;    // d_state handled by these kernels
 constexpr int TS = 8;     // checkpoint stride (tokens)
@@ -52,19 +59,7 @@ constexpr int64_t NUM_CU = 256;
 constexpr int64_t FWD_SLOTS = NUM_CU * 7;
 constexpr int64_t BWD_SLOTS = NUM_CU * 2;
 
-typedef uint16_t bf16_t;
-
 // ------------------------------------------------------------------ io helpers
-__device__ __forceinline__ float to_f(float v) { return v; }
-__device__ __forceinline__ float to_f(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
-
-template <typename T> __device__ __forceinline__ T from_f(float v);
-template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
-// f32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
-template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) {
-    return __builtin_bit_cast(bf16_t, (__bf16)v);
-}
-
 // 16 consecutive values (one B_t or C_t row); the address is wave-uniform.
 __device__ __forceinline__ void load16(const float* __restrict__ p, float v[NS]) {
     const float4* q = reinterpret_cast<const float4*>(p);
@@ -133,12 +128,6 @@ __device__ __forceinline__ float softplus_sig(float u, float& sig) {
                          ? e
                          : (__builtin_amdgcn_logf(w) * LN2) * (e * __builtin_amdgcn_rcpf(wm1));
     return fmaxf(u, 0.0f) + lp;
-}
-
-__device__ __forceinline__ float sigmoid_f(float z) {
-    const float e = __builtin_amdgcn_exp2f(-fabsf(z) * LOG2E);
-    const float r = __builtin_amdgcn_rcpf(1.0f + e);
-    return z >= 0.0f ? r : e * r;
 }
 
 // One token of the recurrence for one channel: h <- exp2(delta*A2) h + (delta x) B,
@@ -856,31 +845,14 @@ BwdWs bwd_ws(const Plan& p) {
     return w;
 }
 
-bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
-
+// Every scan kernel runs 256-thread workgroups.
 struct Launcher {
-    hipStream_t s;
-    ssm_timing* tm;
-    template <typename... KArgs, typename... Args>
-    ssm_status operator()(int kid, void (*kern)(KArgs...), dim3 grid, Args... args) {
-        const bool rec = tm && tm->events && tm->count < tm->capacity && tm->count < SSM_TIMING_MAX;
-        if (rec) (void)hipEventRecord(tm->events[2 * tm->count], s);
-        hipLaunchKernelGGL(kern, grid, dim3(WG), 0, s, args...);
-        const hipError_t e = hipGetLastError();
-        if (rec) {
-            (void)hipEventRecord(tm->events[2 * tm->count + 1], s);
-            tm->kernel_id[tm->count] = kid;
-            tm->count++;
-        }
-        return e == hipSuccess ? SSM_OK : SSM_E_LAUNCH;
+    ssm::Launcher l;
+    template <typename Kern, typename... Args>
+    ssm_status operator()(int kid, Kern kern, dim3 grid, Args... args) {
+        return l(kid, kern, grid, dim3(WG), args...);
     }
 };
-
-#define SSM_TRY(expr)                       \
-    do {                                    \
-        const ssm_status st_ = (expr);      \
-        if (st_ != SSM_OK) return st_;      \
-    } while (0)
 
 template <typename T, bool GATE>
 ssm_status run_fwd(const Plan& p, const void* x, const void* dt, const void* B, const void* C,
@@ -964,7 +936,8 @@ const char* ssm_status_str(ssm_status s) {
         case SSM_E_ALIGN: return "pointer not 16-byte aligned";
         case SSM_E_WORKSPACE: return "workspace too small";
         case SSM_E_LAUNCH: return "kernel launch failed";
-        case SSM_E_UNSUPPORTED: return "unsupported configuration (d_state must be 16, batch <= 65535)";
+        case SSM_E_UNSUPPORTED:
+            return "unsupported configuration (d_state must be 16, d_conv 1..4, batch <= 65535)";
     }
     return "unknown status";
 }
@@ -981,6 +954,11 @@ const char* ssm_kernel_name(int32_t id) {
         case SSM_K_BWD_REDUCE_P: return "k_bwd_reduce_params";
         case SSM_K_STEP: return "k_step";
         case SSM_K_FILL: return "k_fill";
+        case SSM_K_CONV_FWD: return "k_conv_fwd";
+        case SSM_K_CONV_BWD: return "k_conv_bwd";
+        case SSM_K_CONV_BWD_REDUCE: return "k_conv_bwd_reduce";
+        case SSM_K_CONV_STEP: return "k_conv_step";
+        case SSM_K_CONV_RING: return "k_conv_ring";
     }
     return "?";
 }
@@ -1018,7 +996,7 @@ ssm_status ssm_scan_fwd(const ssm_dims* dims, const void* x, const void* dt, con
     const size_t need = fwd_ws(p).total;
     if (p.L > 0 && need > 0 && (!ws || ws_bytes < need)) return SSM_E_WORKSPACE;
     (void)hipGetLastError();
-    Launcher launch{stream, timing};
+    Launcher launch{{stream, timing}};
     if (p.L == 0) {
         if (!h_last) return SSM_OK;
         const int64_t n = p.Bt * p.D * NS;
@@ -1053,7 +1031,7 @@ ssm_status ssm_scan_bwd(const ssm_dims* dims, const void* x, const void* dt, con
     const size_t need = p.L > 0 ? bwd_ws(p).total : 0;
     if (need > 0 && (!ws || ws_bytes < need)) return SSM_E_WORKSPACE;
     (void)hipGetLastError();
-    Launcher launch{stream, timing};
+    Launcher launch{{stream, timing}};
     if (p.L == 0) {
         const int64_t np = p.D * NS;
         SSM_TRY(launch(SSM_K_FILL, k_fill, dim3((unsigned)((np + WG - 1) / WG)), dA_log,
@@ -1090,7 +1068,7 @@ ssm_status ssm_scan_step(int64_t batch, int64_t d_inner, int64_t d_state, int32_
     for (const void* q : ptrs)
         if (q && misaligned(q)) return SSM_E_ALIGN;
     (void)hipGetLastError();
-    Launcher launch{stream, timing};
+    Launcher launch{{stream, timing}};
     const dim3 grid((unsigned)((d_inner + WG - 1) / WG), 1, (unsigned)batch);
     const int Dn = (int)d_inner;
     if (io_dtype == SSM_F32) {

@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI (no GPU needed, nothing is launched):
-the library loads, exports every function include/ssm_scan.h declares, and
-rejects bad arguments with the documented status before any HIP call."""
+the library loads, exports every function include/ssm_scan.h and
+include/ssm_conv1d.h declare, and rejects bad arguments with the documented
+status before any HIP call."""
 import ctypes
 import os
 import re
@@ -8,7 +9,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("ssm_scan.h", "ssm_conv1d.h")]
 
 ssm = pytest.importorskip("selective_state_space_04_amd")
 lib = ssm.library()
@@ -17,18 +18,27 @@ OK, NULLPTR, SHAPE, DTYPE, ALIGN, WORKSPACE, LAUNCH, UNSUPPORTED = range(8)
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssm_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(ssm_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_exports_present():
     names = _declared_functions()
     assert {"ssm_scan_fwd", "ssm_scan_bwd", "ssm_scan_step", "ssm_scan_ckpt_bytes",
             "ssm_scan_fwd_workspace_bytes", "ssm_scan_bwd_workspace_bytes", "ssm_status_str",
-            "ssm_kernel_name"} <= set(names)
+            "ssm_kernel_name", "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_conv1d_step",
+            "ssm_conv1d_bwd_workspace_bytes"} <= set(names)
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in ssm_scan.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in a header but not exported"
+
+
+def test_kernel_names():
+    names = [ssm.kernel_name(i) for i in range(1, 16)]
+    assert "?" not in names and len(set(names)) == 15
+    assert ssm.kernel_name(99) == "?"
 
 
 def test_status_strings():
@@ -139,3 +149,79 @@ def test_binding_rejects_strided_and_mistyped_tensors():
     b = torch.zeros(2, 8, 16, dtype=torch.float64)
     with pytest.raises(TypeError):
         ssm.ssm_scan_fwd(x, x, b, b, None, torch.zeros(4, 16), None, None)
+
+
+def _cdims(b=2, L=64, d=32, k=4, io=0):
+    return ssm.ConvDims(b, L, d, k, io)
+
+
+def test_conv_workspace_size():
+    # partials: one row of (d_conv + 1) sums per channel per (batch, 256-token block)
+    assert lib.ssm_conv1d_bwd_workspace_bytes(ctypes.byref(_cdims(2, 300, 32, 4))) == 4 * 2 * 2 * 32 * 5
+    assert lib.ssm_conv1d_bwd_workspace_bytes(ctypes.byref(_cdims(L=0))) == 0
+    for bad in (_cdims(b=0), _cdims(d=0), _cdims(k=0), _cdims(k=5), _cdims(io=3), _cdims(L=-1)):
+        assert lib.ssm_conv1d_bwd_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_conv_rejects_bad_arguments():
+    P = ctypes.c_void_p
+
+    def fwd(dims, **over):
+        a = dict(x=FAKE, w=FAKE, bias=None, ring0=None, y=FAKE, ring_last=None)
+        a.update(over)
+        keys = ("x", "w", "bias", "ring0", "y", "ring_last")
+        return lib.ssm_conv1d_fwd(ctypes.byref(dims) if dims is not None else None,
+                                  *[P(a[k]) if a[k] else None for k in keys], None, None)
+
+    def bwd(dims, **over):
+        a = dict(x=FAKE, w=FAKE, bias=None, ring0=None, dy=FAKE, dx=FAKE, dw=FAKE, dbias=FAKE,
+                 dring0=None, ws=None, ws_bytes=0)
+        a.update(over)
+        keys = ("x", "w", "bias", "ring0", "dy", "dx", "dw", "dbias", "dring0", "ws")
+        return lib.ssm_conv1d_bwd(ctypes.byref(dims), *[P(a[k]) if a[k] else None for k in keys],
+                                  a["ws_bytes"], None, None)
+
+    def step(b=4, d=32, k=4, io=0, **over):
+        a = dict(ring=FAKE, x=FAKE, w=FAKE, bias=None, y=FAKE)
+        a.update(over)
+        keys = ("ring", "x", "w", "bias", "y")
+        return lib.ssm_conv1d_step(b, d, k, io, *[P(a[k]) if a[k] else None for k in keys], None, None)
+
+    assert fwd(None) == NULLPTR
+    assert fwd(_cdims(b=0)) == SHAPE
+    assert fwd(_cdims(k=0)) == SHAPE
+    assert fwd(_cdims(k=5)) == UNSUPPORTED
+    assert fwd(_cdims(b=70000)) == UNSUPPORTED
+    assert fwd(_cdims(io=2)) == DTYPE
+    assert fwd(_cdims(), x=None) == NULLPTR
+    assert fwd(_cdims(), w=None) == NULLPTR
+    assert fwd(_cdims(), y=FAKE + 2) == ALIGN
+    assert fwd(_cdims(), ring0=FAKE + 4) == ALIGN
+    assert fwd(_cdims(), ring0=FAKE, ring_last=FAKE) == UNSUPPORTED  # in-place ring update
+    d = _cdims()
+    need = lib.ssm_conv1d_bwd_workspace_bytes(ctypes.byref(d))
+    assert bwd(d) == WORKSPACE
+    assert bwd(d, ws=FAKE, ws_bytes=need - 4) == WORKSPACE
+    assert bwd(d, dw=None, ws=FAKE, ws_bytes=need) == NULLPTR
+    assert bwd(d, dbias=None, ws=FAKE, ws_bytes=need) == NULLPTR
+    assert bwd(d, dy=None, ws=FAKE, ws_bytes=need) == NULLPTR
+    assert bwd(d, dx=FAKE + 8, ws=FAKE, ws_bytes=need) == ALIGN
+    assert bwd(_cdims(k=9)) == UNSUPPORTED
+    assert step(b=0) == SHAPE
+    assert step(k=6) == UNSUPPORTED
+    assert step(io=4) == DTYPE
+    assert step(ring=None) == NULLPTR
+    assert step(x=None) == NULLPTR
+    assert step(y=FAKE + 2) == ALIGN
+
+
+def test_conv_binding_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(2, 8, 4).transpose(0, 1)
+    with pytest.raises((ValueError, TypeError)):
+        ssm.ssm_conv1d_fwd(x, torch.zeros(2, 4))
+    x = torch.zeros(2, 8, 4)
+    with pytest.raises(ValueError):
+        ssm.ssm_conv1d_fwd(x, torch.zeros(5, 4))             # w rows != d_inner
+    with pytest.raises(TypeError):
+        ssm.ssm_conv1d_fwd(x, torch.zeros(4, 4, dtype=torch.float64))

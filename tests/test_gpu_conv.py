@@ -1,0 +1,184 @@
+"""GPU parity of the HIP causal depthwise conv1d + SiLU (forward, backward, ring
+step) against the f64 oracle (oracle/conv_oracle.c).
+
+Pass criterion per output tensor, as for the scan:
+    max_i |gpu_i - oracle_i| <= rtol * max_i |oracle_i|
+with rtol = 1e-5 for f32 outputs, 1e-4 for f32 gradients and 2e-2 for every
+output with bf16 activations.  Exact checks: stepping token by token reproduces
+the forward bit for bit, a forward split at any token and continued from its
+ring reproduces the unsplit forward, repeated backward calls are bitwise equal,
+and bf16 outputs are the nearest-even roundings of the f32 path on the same
+values.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+ssm = pytest.importorskip("selective_state_space_04_amd")
+
+pytestmark = pytest.mark.gpu
+
+F32_FWD = 1e-5
+F32_GRAD = 1e-4
+BF16_TOL = 2e-2
+DEV = torch.device("cuda:0")
+
+
+def _t(a, dtype=torch.float32):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dtype)
+
+
+def _np(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def _rel(g, o):
+    g = _np(g) if isinstance(g, torch.Tensor) else g
+    return float(np.max(np.abs(g - o)) / max(float(np.max(np.abs(o))), 1e-30)) if o.size else 0.0
+
+
+def _run(inp, io, want_dring0=True):
+    x, dy = _t(inp["x"], io), _t(inp["dy"], io)
+    w, b, r0 = _t(inp["w"]), _t(inp["bias"]), _t(inp["ring0"])
+    y, ring = ssm.ssm_conv1d_fwd(x, w, b, r0, return_ring=True)
+    g = ssm.ssm_conv1d_bwd(x, w, b, dy, r0, want_dring0=want_dring0)
+    torch.cuda.synchronize()
+    return y, ring, g
+
+
+def _check(inp, io, fwd_tol, grad_tol):
+    k = inp["w"].shape[1]
+    y, ring, g = _run(inp, io)
+    ref = oracle.conv_fwd(inp["x"], inp["w"], inp["bias"], inp["ring0"])
+    gr = oracle.conv_bwd(inp["x"], inp["w"], inp["bias"], inp["dy"], inp["ring0"])
+    errs = {"y": _rel(y, ref["y"])}
+    if k > 1:
+        # the ring holds copies of inputs: exact
+        np.testing.assert_array_equal(_np(ring), ref["s_last"])
+    for n in ("dx", "dw", "dbias") + (("dring0",) if k > 1 else ()):
+        errs[n] = _rel(g[n], gr["ds0" if n == "dring0" else n])
+    assert errs["y"] <= fwd_tol, errs
+    assert all(v <= grad_tol for n, v in errs.items() if n != "y"), errs
+    return errs
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+@pytest.mark.parametrize("ring", [False, True])
+def test_parity_f32_vectorised_channels(k, ring):
+    # d_inner % 4 == 0: four channels per lane; 300 tokens = two 256-token blocks, ragged
+    inp = W.make_conv_inputs(2, 300, 96, k, seed=k, with_ring=ring)
+    _check(inp, torch.float32, F32_FWD, F32_GRAD)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_parity_bf16(k):
+    inp = W.make_conv_inputs(3, 517, 256, k, seed=10 + k, bf16=True, with_ring=True)
+    _check(inp, torch.bfloat16, BF16_TOL, BF16_TOL)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 37), (3, 77, 37), (2, 63, 5), (1, 1000, 100), (2, 2, 3)])
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_parity_ragged(shape, io):
+    # odd d_inner takes the one-channel-per-lane path; L shorter than the window
+    b, L, d = shape
+    bf = io == torch.bfloat16
+    inp = W.make_conv_inputs(b, L, d, 4, seed=L + d, bf16=bf, with_ring=True)
+    tol = (BF16_TOL, BF16_TOL) if bf else (F32_FWD, F32_GRAD)
+    _check(inp, io, *tol)
+
+
+def test_parity_without_bias_or_ring():
+    inp = W.make_conv_inputs(2, 129, 64, 4, seed=3, with_bias=False)
+    x, w, dy = _t(inp["x"]), _t(inp["w"]), _t(inp["dy"])
+    y, _ = ssm.ssm_conv1d_fwd(x, w, None, None)
+    g = ssm.ssm_conv1d_bwd(x, w, None, dy, None, want_dring0=True)
+    torch.cuda.synchronize()
+    ref = oracle.conv_fwd(inp["x"], inp["w"], None)
+    gr = oracle.conv_bwd(inp["x"], inp["w"], None, inp["dy"])
+    assert _rel(y, ref["y"]) <= F32_FWD
+    for n, o in (("dx", "dx"), ("dw", "dw"), ("dbias", "dbias"), ("dring0", "ds0")):
+        assert _rel(g[n], gr[o]) <= F32_GRAD, n
+
+
+def test_bench_workload_full_parity():
+    """The full 4 x 8192 x 5120 bf16 workload, every output against the oracle."""
+    inp = W.make_conv_config("conv_mamba2p8b_bf16")
+    inp["bias"] = W.make_conv_inputs(1, 1, 5120, 4, seed=5)["bias"]  # exercise the bias too
+    errs = _check(inp, torch.bfloat16, BF16_TOL, BF16_TOL)
+    print("conv bench workload errors", errs)
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("k", [2, 4])
+def test_step_chain_equals_forward_bitwise(io, k):
+    inp = W.make_conv_inputs(4, 40, 128, k, seed=7, bf16=io == torch.bfloat16, with_ring=True)
+    x, w, b = _t(inp["x"], io), _t(inp["w"]), _t(inp["bias"])
+    r0 = _t(inp["ring0"])
+    y_full, ring_full = ssm.ssm_conv1d_fwd(x, w, b, r0, return_ring=True)
+    ring = r0.clone()
+    ys = [ssm.ssm_conv1d_step(ring, x[:, t].contiguous(), w, b) for t in range(x.shape[1])]
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(ys, dim=1), y_full)
+    assert torch.equal(ring, ring_full)
+    # and the step agrees with the oracle's step
+    rr = inp["ring0"].astype(np.float64).copy()
+    yo = np.stack([oracle.conv_step(rr, inp["x"][:, t], inp["w"], inp["bias"]) for t in range(x.shape[1])], 1)
+    assert _rel(torch.stack(ys, dim=1), yo) <= (BF16_TOL if io == torch.bfloat16 else F32_FWD)
+
+
+def test_step_width_one_needs_no_ring():
+    inp = W.make_conv_inputs(2, 3, 64, 1, seed=2)
+    x, w, b = _t(inp["x"]), _t(inp["w"]), _t(inp["bias"])
+    y_full, _ = ssm.ssm_conv1d_fwd(x, w, b)
+    ys = torch.stack([ssm.ssm_conv1d_step(None, x[:, t].contiguous(), w, b) for t in range(3)], dim=1)
+    torch.cuda.synchronize()
+    assert torch.equal(ys, y_full)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 255, 256, 300])
+def test_split_forward_with_ring_is_exact(split):
+    inp = W.make_conv_inputs(2, 520, 64, 4, seed=9, with_ring=True)
+    x, w, b, r0 = _t(inp["x"]), _t(inp["w"]), _t(inp["bias"]), _t(inp["ring0"])
+    y_full, ring_full = ssm.ssm_conv1d_fwd(x, w, b, r0, return_ring=True)
+    ya, ra = ssm.ssm_conv1d_fwd(x[:, :split].contiguous(), w, b, r0, return_ring=True)
+    yb, rb = ssm.ssm_conv1d_fwd(x[:, split:].contiguous(), w, b, ra, return_ring=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([ya, yb], dim=1), y_full)
+    assert torch.equal(rb, ring_full)
+
+
+def test_seqlen_zero():
+    inp = W.make_conv_inputs(2, 0, 32, 4, seed=1, with_ring=True)
+    x = torch.empty(2, 0, 32, device=DEV)
+    w, b, r0 = _t(inp["w"]), _t(inp["bias"]), _t(inp["ring0"])
+    y, ring = ssm.ssm_conv1d_fwd(x, w, b, r0, return_ring=True)
+    g = ssm.ssm_conv1d_bwd(x, w, b, torch.empty_like(x), r0, want_dring0=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ring, r0)
+    _, ring_z = ssm.ssm_conv1d_fwd(x, w, b, None, return_ring=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ring_z) == 0
+    for n in ("dw", "dbias", "dring0"):
+        assert torch.count_nonzero(g[n]) == 0, n
+
+
+def test_backward_is_deterministic():
+    inp = W.make_conv_inputs(4, 1500, 512, 4, seed=4, bf16=True, with_ring=True)
+    _, _, g1 = _run(inp, torch.bfloat16)
+    _, _, g2 = _run(inp, torch.bfloat16)
+    for n in ("dx", "dw", "dbias", "dring0"):
+        assert torch.equal(g1[n], g2[n]), n
+
+
+def test_bf16_outputs_are_nearest_even_roundings_of_the_f32_path():
+    inp = W.make_conv_inputs(2, 700, 160, 4, seed=6, bf16=True, with_ring=True)
+    y32, _, g32 = _run(inp, torch.float32)
+    y16, _, g16 = _run(inp, torch.bfloat16)
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+    assert torch.equal(g16["dx"], g32["dx"].to(torch.bfloat16))
+    # parameter gradients are f32 sums of the same per-token products
+    assert torch.equal(g16["dw"], g32["dw"])
+    assert torch.equal(g16["dbias"], g32["dbias"])

@@ -104,3 +104,37 @@ def random_a_log(d_inner, d_state=D_STATE, *, seed=1, spread=0.5):
     rng = np.random.default_rng(seed)
     base = np.log(np.arange(1, d_state + 1, dtype=np.float64))[None, :]
     return (base + spread * rng.standard_normal((d_inner, d_state))).astype(np.float32)
+
+
+# Causal depthwise conv1d + SiLU in front of the scan: same batch/seqlen/d_inner
+# as the bench workload, kernel width 4.
+CONV_CONFIGS = {
+    "conv_mamba2p8b_bf16": dict(batch=4, seqlen=8192, d_inner=5120, d_conv=4, io="bf16"),
+}
+
+
+def make_conv_inputs(batch, seqlen, d_inner, d_conv=4, *, seed=0, bf16=False, with_ring=False,
+                     with_bias=True):
+    """Inputs of the conv1d + SiLU.  Draw order from default_rng(seed), each
+    standard_normal(float32): x [batch, seqlen, d_inner], w [d_inner, d_conv]
+    (scaled by 1/sqrt(d_conv), the fan-in of a depthwise tap row), bias [d_inner]
+    (scaled by 0.5; zero when with_bias is False, the canonical zero conv bias),
+    ring0 [batch, d_inner, d_conv-1], dy [batch, seqlen, d_inner].  Every tensor is
+    drawn whatever the flags, so the flags do not shift the stream.  With bf16 the
+    activations (x, ring0, dy) are rounded to nearest-even bf16."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, seqlen, d_inner), dtype=np.float32)
+    w = rng.standard_normal((d_inner, d_conv), dtype=np.float32) * np.float32(1.0 / math.sqrt(d_conv))
+    bias = rng.standard_normal(d_inner, dtype=np.float32) * np.float32(0.5)
+    ring0 = rng.standard_normal((batch, d_inner, max(d_conv - 1, 0)), dtype=np.float32)
+    dy = rng.standard_normal((batch, seqlen, d_inner), dtype=np.float32)
+    if bf16:
+        x, ring0, dy = round_bf16(x), round_bf16(ring0), round_bf16(dy)
+    return {"x": x, "w": w, "bias": bias if with_bias else np.zeros(d_inner, np.float32),
+            "ring0": ring0 if with_ring and d_conv > 1 else None, "dy": dy}
+
+
+def make_conv_config(name, *, seed=0):
+    c = CONV_CONFIGS[name]
+    return make_conv_inputs(c["batch"], c["seqlen"], c["d_inner"], c["d_conv"], seed=seed,
+                            bf16=c["io"] == "bf16", with_bias=False)
