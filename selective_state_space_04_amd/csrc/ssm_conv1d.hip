@@ -37,14 +37,16 @@ namespace {
 using ssm::bf16_t;
 using ssm::from_f;
 using ssm::misaligned;
-using ssm::sigmoid_f;
 using ssm::to_f;
 
 constexpr int WG = 256;  // 64 lanes (channel groups) x 4 waves (token runs)
 constexpr int NWAVE = WG / 64;
 constexpr int TT = 64;   // tokens per wave
-constexpr int PF = 8;    // tokens fetched ahead
+constexpr int PF = 4;    // tokens fetched ahead
 constexpr int KMAX = 4;
+// The backward's unrolled path runs its TT tokens in groups of PF and ends with
+// exactly one group that mixes the run's last tokens and the K-1 look-ahead.
+static_assert(TT % PF == 0 && PF >= KMAX, "token run must split into groups of PF >= KMAX");
 
 // ---------------------------------------------------------------- VEC channels
 template <typename T, int VEC> struct Raw;
@@ -85,6 +87,13 @@ template <> __device__ __forceinline__ void st<bf16_t, 1>(bf16_t* p, const float
     p[0] = from_f<bf16_t>(v[0]);
 }
 
+// sigmoid(p) = 1 / (1 + exp(-p)) with the hardware exp2 and reciprocal.  No sign
+// folding is needed here: for p << 0 the exponential is large and its
+// reciprocal stays relatively accurate, and past overflow 1/inf gives 0.
+__device__ __forceinline__ float sigmoid_c(float p) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p * -1.4426950408889634f));
+}
+
 // pre-activation of one channel: bias first, then the taps in increasing k.
 template <int K>
 __device__ __forceinline__ float conv_pre(float bias, const float w[K], const float v[K]) {
@@ -94,76 +103,97 @@ __device__ __forceinline__ float conv_pre(float bias, const float w[K], const fl
     return acc;
 }
 
-// Per-lane setup shared by the forward and backward: weights, bias, and the K-1
-// inputs before token t0 (from x, or from the ring / zero before the sequence).
-template <typename T, int K, int VEC>
-__device__ __forceinline__ void conv_prologue(const T* __restrict__ x, const float* __restrict__ w,
-                                              const float* __restrict__ bias,
-                                              const float* __restrict__ ring0, int b, int c0, int t0,
-                                              int L, int D, float wk[VEC][K], float bs[VEC],
-                                              float win[K][VEC]) {
+template <int K, int VEC>
+__device__ __forceinline__ void load_params(const float* __restrict__ w, const float* __restrict__ bias,
+                                            int c0, float wk[VEC][K], float bs[VEC]) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
 #pragma unroll
         for (int k = 0; k < K; ++k) wk[v][k] = w[(int64_t)(c0 + v) * K + k];
         bs[v] = bias ? bias[c0 + v] : 0.0f;
     }
+}
+
+// Input of one lane's VEC channels at time tau < L: x for tau >= 0, else the
+// caller's ring (zero when absent).
+template <typename T, int K, int VEC>
+__device__ __forceinline__ void input_at(const T* __restrict__ x, const float* __restrict__ ring0, int b,
+                                         int c0, int tau, int L, int D, float out[VEC]) {
+    if (tau >= 0) {
+        unpack(ld<T, VEC>(x + ((int64_t)b * L + tau) * D + c0), out);
+    } else {
 #pragma unroll
-    for (int j = 0; j < K - 1; ++j) {
-        const int tau = t0 - (K - 1) + j;
-        if (tau >= 0) {
-            unpack(ld<T, VEC>(x + ((int64_t)b * L + tau) * D + c0), win[j]);
-        } else {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v)
-                win[j][v] = ring0 ? ring0[((int64_t)b * D + c0 + v) * (K - 1) + (tau + K - 1)] : 0.0f;
-        }
+        for (int v = 0; v < VEC; ++v)
+            out[v] = ring0 ? ring0[((int64_t)b * D + c0 + v) * (K - 1) + (tau + K - 1)] : 0.0f;
     }
 }
 
+// Drop the oldest of N window entries (the caller then writes entry N-1).
+template <int N, int VEC>
+__device__ __forceinline__ void shift_window(float win[N][VEC]) {
+#pragma unroll
+    for (int j = 0; j + 1 < N; ++j)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) win[j][v] = win[j + 1][v];
+}
+
 // ------------------------------------------------------------------ forward
+// One output token from the window of its K inputs (oldest first).
+template <typename T, int K, int VEC>
+__device__ __forceinline__ void fwd_token(const float wk[VEC][K], const float bs[VEC],
+                                          const float win[K][VEC], T* __restrict__ yrow) {
+    float out[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        float tap[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) tap[k] = win[k][v];
+        const float pre = conv_pre<K>(bs[v], wk[v], tap);
+        out[v] = pre * sigmoid_c(pre);
+    }
+    st<T, VEC>(yrow, out);
+}
+
 template <typename T, int K, int VEC>
 __global__ __launch_bounds__(WG) void k_conv_fwd(const T* __restrict__ x, const float* __restrict__ w,
                                                  const float* __restrict__ bias,
                                                  const float* __restrict__ ring0, T* __restrict__ y,
                                                  float* __restrict__ ring_last, int L, int D) {
     typedef typename Raw<T, VEC>::type R;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is uniform across the wave: say so, so that every token-range
+    // test below is a scalar branch instead of an exec-mask region
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c0 = (blockIdx.x * 64 + lane) * VEC;
     const int b = blockIdx.z;
     const int t0 = (blockIdx.y * NWAVE + wave) * TT;
     if (c0 >= D || t0 >= L) return;  // no barrier in this kernel
     const int t1 = min(t0 + TT, L);
     float wk[VEC][K], bs[VEC], win[K][VEC];
-    conv_prologue<T, K, VEC>(x, w, bias, ring0, b, c0, t0, L, D, wk, bs, win);
+    load_params<K, VEC>(w, bias, c0, wk, bs);
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) input_at<T, K, VEC>(x, ring0, b, c0, t0 - (K - 1) + j, L, D, win[j]);
     const T* xp = x + (int64_t)b * L * D + c0;
     T* yp = y + (int64_t)b * L * D + c0;
-    R q[PF];
+    if (t1 - t0 == TT) {
+        // whole run inside the sequence: PF tokens in flight, no range tests in
+        // the body, so the window rotates through registers without copies
+        R q[PF];
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (t0 + p < t1) q[p] = ld<T, VEC>(xp + (int64_t)(t0 + p) * D);
-    for (int u = t0; u < t1; u += PF) {
+        for (int p = 0; p < PF; ++p) q[p] = ld<T, VEC>(xp + (int64_t)(t0 + p) * D);
+        for (int u = t0; u < t1; u += PF) {
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int uu = u + p;
-            if (uu < t1) {
+            for (int p = 0; p < PF; ++p) {
                 unpack(q[p], win[K - 1]);
-                if (uu + PF < t1) q[p] = ld<T, VEC>(xp + (int64_t)(uu + PF) * D);
-                float out[VEC];
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    float tap[K];
-#pragma unroll
-                    for (int k = 0; k < K; ++k) tap[k] = win[k][v];
-                    const float pre = conv_pre<K>(bs[v], wk[v], tap);
-                    out[v] = pre * sigmoid_f(pre);
-                }
-                st<T, VEC>(yp + (int64_t)uu * D, out);
-#pragma unroll
-                for (int j = 0; j < K - 1; ++j)
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) win[j][v] = win[j + 1][v];
+                if (u + p + PF < t1) q[p] = ld<T, VEC>(xp + (int64_t)(u + p + PF) * D);
+                fwd_token<T, K, VEC>(wk, bs, win, yp + (int64_t)(u + p) * D);
+                shift_window<K, VEC>(win);
             }
+        }
+    } else {
+        for (int u = t0; u < t1; ++u) {
+            unpack(ld<T, VEC>(xp + (int64_t)u * D), win[K - 1]);
+            fwd_token<T, K, VEC>(wk, bs, win, yp + (int64_t)u * D);
+            shift_window<K, VEC>(win);
         }
     }
     // the last K-1 inputs (oldest first) continue the stream
@@ -177,6 +207,60 @@ __global__ __launch_bounds__(WG) void k_conv_fwd(const T* __restrict__ x, const 
 }
 
 // ------------------------------------------------------------------ backward
+// g = dy * d silu / d pre at one token, from the window of its K inputs.
+template <int K, int VEC>
+__device__ __forceinline__ void silu_grad(const float wk[VEC][K], const float bs[VEC],
+                                          const float (*taps)[VEC], const float dyv[VEC], float g[VEC]) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        float tap[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) tap[k] = taps[k][v];
+        const float pre = conv_pre<K>(bs[v], wk[v], tap);
+        const float s = sigmoid_c(pre);
+        g[v] = dyv[v] * (s * __builtin_fmaf(pre, 1.0f - s, 1.0f));  // s (1 + pre (1 - s))
+    }
+}
+
+// One step of the backward sweep: token u enters (input xn, upstream dyn; HAVE =
+// u < L, else its g is 0).  Windows before the step: xw[i] = x[u-K+i] and
+// gw[i] = g[u-K+i] (i = 1 .. K-1); after it they end at token u.  Then
+//   own token (u inside this run):  dw[k] += g[u] x[u-K+1+k],  dbias += g[u]
+//   STORE (tau = u-K+1 inside this run):  dx[tau] = sum_k w[k] g[tau+K-1-k]
+template <typename T, int K, int VEC>
+__device__ __forceinline__ void bwd_step(const float wk[VEC][K], const float bs[VEC], float xw[K][VEC],
+                                         float gw[K][VEC], bool have, bool own, bool store,
+                                         const float xn[VEC], const float dyn[VEC], float dwa[K][VEC],
+                                         float dba[VEC], T* __restrict__ dxrow) {
+    shift_window<K, VEC>(xw);
+    shift_window<K, VEC>(gw);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) xw[K - 1][v] = xn[v];
+    float g[VEC];
+    silu_grad<K, VEC>(wk, bs, xw, dyn, g);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) gw[K - 1][v] = have ? g[v] : 0.0f;
+    if (own) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            dba[v] += gw[K - 1][v];
+#pragma unroll
+            for (int k = 0; k < K; ++k) dwa[k][v] = __builtin_fmaf(gw[K - 1][v], xw[k][v], dwa[k][v]);
+        }
+    }
+    if (store) {
+        float o[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) acc = __builtin_fmaf(wk[v][k], gw[K - 1 - k][v], acc);
+            o[v] = acc;
+        }
+        st<T, VEC>(dxrow, o);
+    }
+}
+
 // part: [Bt * gridDim.y, D, K+1] per-workgroup sums (dw taps, then dbias).
 template <typename T, int K, int VEC>
 __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const float* __restrict__ w,
@@ -188,7 +272,7 @@ __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const 
     typedef typename Raw<T, VEC>::type R;
     constexpr int NP = (K + 1) * VEC;
     __shared__ float red[NWAVE][NP][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c0 = (blockIdx.x * 64 + lane) * VEC;
     const int b = blockIdx.z;
     const int t0 = (blockIdx.y * NWAVE + wave) * TT;
@@ -201,103 +285,103 @@ __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const 
     }
     if (c0 < D && t0 < L) {
         const int t1 = min(t0 + TT, L);
-        const int uend = t1 + K - 1;  // g is needed K-1 tokens past the run
-        const int lend = min(uend, L);  // tokens that exist
-        float wk[VEC][K], bs[VEC], win[K][VEC], gw[K][VEC], dr[KMAX][VEC];
-        conv_prologue<T, K, VEC>(x, w, bias, ring0, b, c0, t0, L, D, wk, bs, win);
+        float wk[VEC][K], bs[VEC], xw[K][VEC], gw[K][VEC];
+        load_params<K, VEC>(w, bias, c0, wk, bs);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
+        for (int i = 1; i < K; ++i) input_at<T, K, VEC>(x, ring0, b, c0, t0 - K + i, L, D, xw[i]);
 #pragma unroll
-            for (int k = 0; k < K; ++k) gw[k][v] = 0.0f;
+        for (int i = 0; i < K; ++i)
 #pragma unroll
-            for (int j = 0; j < KMAX; ++j) dr[j][v] = 0.0f;
-        }
+            for (int v = 0; v < VEC; ++v) gw[i][v] = 0.0f;
         const int64_t base = (int64_t)b * L * D + c0;
         const T* xp = x + base;
         const T* gp = dy + base;
         T* dxp = dx + base;
-        R qx[PF], qg[PF];
-#pragma unroll
-        for (int p = 0; p < PF; ++p)
-            if (t0 + p < lend) {
-                qx[p] = ld<T, VEC>(xp + (int64_t)(t0 + p) * D);
-                qg[p] = ld<T, VEC>(gp + (int64_t)(t0 + p) * D);
-            }
-        for (int u = t0; u < uend; u += PF) {
-#pragma unroll
-            for (int p = 0; p < PF; ++p) {
-                const int uu = u + p;
-                if (uu < uend) {
-                    float g[VEC];
-                    if (uu < L) {
-                        float dyv[VEC];
-                        unpack(qx[p], win[K - 1]);
-                        unpack(qg[p], dyv);
-                        if (uu + PF < lend) {
-                            qx[p] = ld<T, VEC>(xp + (int64_t)(uu + PF) * D);
-                            qg[p] = ld<T, VEC>(gp + (int64_t)(uu + PF) * D);
-                        }
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) {
-                            float tap[K];
-#pragma unroll
-                            for (int k = 0; k < K; ++k) tap[k] = win[k][v];
-                            const float pre = conv_pre<K>(bs[v], wk[v], tap);
-                            const float s = sigmoid_f(pre);
-                            // d silu / d pre = s * (1 + pre * (1 - s))
-                            g[v] = dyv[v] * (s * __builtin_fmaf(pre, 1.0f - s, 1.0f));
-                        }
-                    } else {
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) g[v] = 0.0f;
-                    }
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) gw[K - 1][v] = g[v];
-                    if (uu < t1) {  // this run's own tokens
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) {
-                            dba[v] += g[v];
-#pragma unroll
-                            for (int k = 0; k < K; ++k) dwa[k][v] = __builtin_fmaf(g[v], win[k][v], dwa[k][v]);
-                        }
-                    }
-                    // taps before the sequence: input time j-(K-1) of the ring
-                    if (uu < K - 1) {
-#pragma unroll
-                        for (int j = 0; j < K - 1; ++j)
-                            if (j >= uu)
-#pragma unroll
-                                for (int v = 0; v < VEC; ++v)
-                                    dr[j][v] = __builtin_fmaf(wk[v][j - uu], g[v], dr[j][v]);
-                    }
-                    const int tau = uu - (K - 1);
-                    if (tau >= t0) {
-                        float o[VEC];
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) {
-                            float acc = 0.0f;
-#pragma unroll
-                            for (int k = 0; k < K; ++k) acc = __builtin_fmaf(wk[v][k], gw[K - 1 - k][v], acc);
-                            o[v] = acc;
-                        }
-                        st<T, VEC>(dxp + (int64_t)tau * D, o);
-                    }
-#pragma unroll
-                    for (int j = 0; j < K - 1; ++j)
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) {
-                            win[j][v] = win[j + 1][v];
-                            gw[j][v] = gw[j + 1][v];
-                        }
-                }
-            }
-        }
-        if (t0 == 0 && dring0) {
+        // a run whose K-1 token look-ahead also lies inside the sequence takes the
+        // unrolled path below after its first K-1 tokens
+        // ring entry j (input time j-(K-1)) feeds tokens 0..j through tap j-t; it
+        // is final once gw[t+1] = g[t] for t = 0 .. K-2 (after token K-2 entered)
+        auto ring_grad = [&]() {
 #pragma unroll
             for (int v = 0; v < VEC; ++v)
 #pragma unroll
-                for (int j = 0; j < K - 1; ++j)
-                    dring0[((int64_t)b * D + c0 + v) * (K - 1) + j] = dr[j][v];
+                for (int j = 0; j < K - 1; ++j) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int t = 0; t <= j; ++t) acc = __builtin_fmaf(wk[v][j - t], gw[t + 1][v], acc);
+                    dring0[((int64_t)b * D + c0 + v) * (K - 1) + j] = acc;
+                }
+        };
+        const int uend = t1 + K - 1;  // tokens entering: the run plus the look-ahead
+        if (t1 - t0 == TT && t1 + K - 1 <= L) {
+            // The run and its K-1 token look-ahead lie inside the sequence.  The
+            // first K-1 tokens (no dx yet) and the first PF of the rest are fetched
+            // together; the rest stream with PF tokens in flight and no range test
+            // in the bodies, so both windows rotate through registers.
+            const int ugen = t0 + K - 1;
+            const int ulast = uend - 1;
+            R hx[K > 1 ? K - 1 : 1], hg[K > 1 ? K - 1 : 1], qx[PF], qg[PF];
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i) {
+                hx[i] = ld<T, VEC>(xp + (int64_t)(t0 + i) * D);
+                hg[i] = ld<T, VEC>(gp + (int64_t)(t0 + i) * D);
+            }
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                qx[p] = ld<T, VEC>(xp + (int64_t)(ugen + p) * D);
+                qg[p] = ld<T, VEC>(gp + (int64_t)(ugen + p) * D);
+            }
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i) {
+                float xn[VEC], dyn[VEC];
+                unpack(hx[i], xn);
+                unpack(hg[i], dyn);
+                bwd_step<T, K, VEC>(wk, bs, xw, gw, true, true, false, xn, dyn, dwa, dba, dxp);
+            }
+            if (t0 == 0 && dring0) ring_grad();
+            int u0 = ugen;
+            for (; u0 + PF <= t1; u0 += PF) {  // groups of own tokens
+#pragma unroll
+                for (int p = 0; p < PF; ++p) {
+                    const int u = u0 + p;
+                    float xn[VEC], dyn[VEC];
+                    unpack(qx[p], xn);
+                    unpack(qg[p], dyn);
+                    if (u + PF <= ulast) {
+                        qx[p] = ld<T, VEC>(xp + (int64_t)(u + PF) * D);
+                        qg[p] = ld<T, VEC>(gp + (int64_t)(u + PF) * D);
+                    }
+                    bwd_step<T, K, VEC>(wk, bs, xw, gw, true, true, true, xn, dyn, dwa, dba,
+                                        dxp + (int64_t)(u - (K - 1)) * D);
+                }
+            }
+            if (u0 < uend) {  // the last own tokens and the look-ahead: exactly PF steps
+#pragma unroll
+                for (int p = 0; p < PF; ++p) {
+                    const int u = u0 + p;
+                    float xn[VEC], dyn[VEC];
+                    unpack(qx[p], xn);
+                    unpack(qg[p], dyn);
+                    bwd_step<T, K, VEC>(wk, bs, xw, gw, true, u < t1, true, xn, dyn, dwa, dba,
+                                        dxp + (int64_t)(u - (K - 1)) * D);
+                }
+            }
+        } else {
+            for (int u = t0; u < uend; ++u) {
+                const bool have = u < L;
+                float xn[VEC], dyn[VEC];
+                if (have) {
+                    unpack(ld<T, VEC>(xp + (int64_t)u * D), xn);
+                    unpack(ld<T, VEC>(gp + (int64_t)u * D), dyn);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) xn[v] = dyn[v] = 0.0f;
+                }
+                const int tau = u - (K - 1);
+                bwd_step<T, K, VEC>(wk, bs, xw, gw, have, u < t1, tau >= t0, xn, dyn, dwa, dba,
+                                    dxp + (int64_t)max(tau, 0) * D);
+                if (u == K - 2 && t0 == 0 && dring0) ring_grad();
+            }
         }
     }
     // dw / dbias: this lane's sums over its run, then over the 4 runs in order
@@ -316,19 +400,38 @@ __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const 
     }
 }
 
-// dw[d,k] / dbias[d] = sum over tiles (fixed order) of the partials.
+// dw[d,k] / dbias[d] = sum over tiles of the partials, in a fixed order: each of
+// the 4 waves sums a contiguous quarter of the tiles for 64 consecutive outputs
+// (8 loads in flight per lane), then the quarters are added in order.
 __global__ __launch_bounds__(WG) void k_conv_bwd_reduce(const float* __restrict__ part,
                                                         float* __restrict__ dw,
                                                         float* __restrict__ dbias, int64_t ntiles,
                                                         int D, int K) {
-    const int64_t idx = (int64_t)blockIdx.x * WG + threadIdx.x;
+    __shared__ float q[NWAVE][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t per = (int64_t)D * (K + 1);
-    if (idx >= per) return;
+    const int64_t idx = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t n0 = ntiles * wave / NWAVE, n1 = ntiles * (wave + 1) / NWAVE;
     float s = 0.0f;
-    for (int64_t t = 0; t < ntiles; ++t) s += part[t * per + idx];
-    const int d = (int)(idx / (K + 1)), k = (int)(idx % (K + 1));
-    if (k < K) dw[(int64_t)d * K + k] = s;
-    else dbias[d] = s;
+    if (idx < per) {
+        int64_t t = n0;
+        for (; t + 8 <= n1; t += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = part[(t + j) * per + idx];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += v[j];
+        }
+        for (; t < n1; ++t) s += part[t * per + idx];
+    }
+    q[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && idx < per) {
+        const float tot = ((q[0][lane] + q[1][lane]) + q[2][lane]) + q[3][lane];
+        const int d = (int)(idx / (K + 1)), k = (int)(idx % (K + 1));
+        if (k < K) dw[(int64_t)d * K + k] = tot;
+        else dbias[d] = tot;
+    }
 }
 
 // ------------------------------------------------------------------ step
@@ -349,7 +452,7 @@ __global__ __launch_bounds__(WG) void k_conv_step(float* __restrict__ ring, cons
     for (int k = 0; k < K - 1; ++k) tap[k] = r[k];
     tap[K - 1] = xv;
     const float pre = conv_pre<K>(bias ? bias[d] : 0.0f, wk, tap);
-    y[i] = from_f<T>(pre * sigmoid_f(pre));
+    y[i] = from_f<T>(pre * sigmoid_c(pre));
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) r[j] = tap[j + 1];
 }
@@ -419,7 +522,7 @@ ssm_status run_bwd(const ConvPlan& p, const void* x, const float* w, const float
                    dim3((unsigned)p.gx, (unsigned)p.gy, (unsigned)p.Bt), (const T*)x, w, bias, ring0,
                    (const T*)dy, (T*)dx, dring0, part, (int)p.L, (int)p.D));
     const int64_t per = p.D * (p.K + 1);
-    return launch(SSM_K_CONV_BWD_REDUCE, k_conv_bwd_reduce, dim3((unsigned)((per + WG - 1) / WG)),
+    return launch(SSM_K_CONV_BWD_REDUCE, k_conv_bwd_reduce, dim3((unsigned)((per + 63) / 64)),
                   (const float*)part, dw, dbias, p.Bt * p.gy, (int)p.D, (int)p.K);
 }
 
