@@ -30,8 +30,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 F32_VECTOR_PEAK_TFLOPS = 157.3
-KERNEL_SRC = os.path.join(ROOT, "selective_state_space_04_amd", "csrc", "ssm_scan.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c4_mamba2p8b_bf16_traffic.txt")
+CSRC = os.path.join(ROOT, "selective_state_space_04_amd", "csrc")
+# (kernel source, committed counter summary) per workload
+TRAFFIC = {"scan": (os.path.join(CSRC, "ssm_scan.hip"),
+                    os.path.join(ROOT, "profiles", "c4_mamba2p8b_bf16_traffic.txt")),
+           "conv1d": (os.path.join(CSRC, "ssm_conv1d.hip"),
+                      os.path.join(ROOT, "profiles", "conv_mamba2p8b_bf16_traffic.txt"))}
 
 # Algorithmic f32 flops per element (b,t,d,n), FMA = 2, mul/add/exp = 1.
 #  forward main : exp(dt*A) (mul + exp), dt*x*B (mul), h update (FMA), C.h (FMA)  = 7
@@ -75,13 +79,14 @@ def algorithmic_bytes(cfg, esz):
     return {"fwd": fwd, "bwd": bwd, "bwd_main": bwd_main, "fwd_main": fwd}
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, op="scan"):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None
     when the summary was taken on a different kernel source."""
     import hashlib
+    src_path, traffic_path = TRAFFIC[op]
     try:
-        lines = open(TRAFFIC_FILE).read().split("\n")
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        lines = open(traffic_path).read().split("\n")
+        src = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
     except OSError:
         return None
     kv = {}
@@ -115,6 +120,17 @@ def cpu_baseline(inp, cfg, rows, channels):
                       f"the same workload, fwd+bwd in f64 ({elems} elements, {sec:.1f} s)"}
 
 
+def copy_probe(dev):
+    """A plain 1 GiB device-to-device copy: known bytes for calibrating the
+    profiler's FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def conv_bench(args):
     """Causal depthwise conv1d + SiLU, forward + backward, on the conv workload."""
     import numpy as np
@@ -144,6 +160,9 @@ def conv_bench(args):
         ssm.ssm_conv1d_fwd(x, w, bias, y=y, timing=timer)
         ssm.ssm_conv1d_bwd(x, w, bias, dy, out=grads, timing=timer)
 
+    if args.copy_probe:
+        copy_probe(dev)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -168,6 +187,7 @@ def conv_bench(args):
               "k_conv_bwd": btd * esz * 3 + 4 * D * (K + 1)}
     dominant = max(kbytes, key=lambda k: kavg.get(k, 0.0))
     gbps = kbytes[dominant] / (kavg[dominant] * 1e-3) / 1e9
+    traffic = measured_traffic(dominant, "conv1d")
     line = {
         "metric": "causal depthwise conv1d+SiLU fwd+bwd elements(B\u00b7L\u00b7D)/s and achieved HBM GB/s",
         "value": btd / (ms * 1e-3),
@@ -181,8 +201,9 @@ def conv_bench(args):
         "achieved_hbm_GBps": round(sum(kbytes.values()) / (ms * 1e-3) / 1e9, 1),
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kavg.items())},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dominant,
-                     "kernel_ms": round(kavg[dominant], 4), "algorithmic_bytes_per_launch": kbytes[dominant]},
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dominant,
+                     "kernel_ms": round(kavg[dominant], 4), "algorithmic_bytes_per_launch": kbytes[dominant],
+                     "measured_GBps": None if traffic is None else round(traffic / (kavg[dominant] * 1e-3) / 1e9, 1)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -249,11 +270,7 @@ def main():
                          t["dy"], out=grads, timing=timer)
 
     if args.copy_probe:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(dev)
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
