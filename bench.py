@@ -59,9 +59,11 @@ def parse():
     ap.add_argument("--cpu-sample-channels", type=int, default=0,
                     help="channels the oracle baseline runs on (0 = all)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
-    ap.add_argument("--op", choices=("scan", "conv1d"), default="scan",
+    ap.add_argument("--op", choices=("scan", "conv1d", "decode"), default="scan",
                     help="scan: the selective scan fwd+bwd (default); conv1d: the causal depthwise "
-                         "conv1d + SiLU fwd+bwd in front of it, on the same batch/seqlen/d_inner")
+                         "conv1d + SiLU fwd+bwd in front of it, on the same batch/seqlen/d_inner; "
+                         "decode: 1024 single-token steps at batch 256 x d_inner 5120, eager and "
+                         "replayed from a captured HIP graph")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to calibrate "
                          "profiler FETCH_SIZE / WRITE_SIZE counters")
@@ -226,6 +228,122 @@ def conv_bench(args):
             f.write(s + "\n")
 
 
+def decode_bench(args):
+    """1024 consecutive ssm_scan_step calls from a zero state (batch 256, d_inner
+    5120, f32 with bf16-representable values): timed eagerly, and as one captured
+    HIP graph of all 1024 launches, whose every replay is checked against the
+    eager result."""
+    import numpy as np
+    import torch
+
+    import selective_state_space_04_amd as ssm
+    import workloads as W
+
+    name = "c5_decode_step"
+    cfg = W.CONFIGS[name]
+    dev = torch.device("cuda:0")
+    B, L, D, N = cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"]
+    print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
+    inp = W.make_config(name, with_dy=False)
+    # time-major on the device, so that every step reads contiguous [batch, ...] slices
+    tm = {k: torch.from_numpy(inp[k]).to(dev).transpose(0, 1).contiguous() for k in ("x", "z", "dt", "B", "C")}
+    del inp["x"], inp["z"], inp["dt"]
+    A_log, Dp, bias = (torch.from_numpy(inp[k]).to(dev) for k in ("A_log", "D", "dt_bias"))
+    h = torch.zeros(B, D, N, device=dev)
+    ys = torch.empty(L, B, D, device=dev)
+
+    def run():
+        for t in range(L):
+            ssm.ssm_scan_step(h, tm["x"][t], tm["dt"][t], tm["B"][t], tm["C"][t], tm["z"][t], A_log, Dp, bias,
+                              y=ys[t])
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        out = []
+        for _ in range(reps):
+            h.zero_()
+            torch.cuda.synchronize()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return float(np.median(out))
+
+    h.zero_()
+    run()  # warm-up
+    torch.cuda.synchronize()
+    eager_ms = timed(run, max(1, min(args.steps, 5)))
+    y_ref, h_ref = ys.clone(), h.clone()
+    # one step kernel per launch, timed by the library's own events over 16 steps
+    tmr = ssm.LaunchTimer()
+    h.zero_()
+    for t in range(tmr.capacity):
+        ssm.ssm_scan_step(h, tm["x"][t], tm["dt"][t], tm["B"][t], tm["C"][t], tm["z"][t], A_log, Dp, bias,
+                          y=ys[t], timing=tmr)
+    torch.cuda.synchronize()
+    kernel_ms = float(np.mean([ms for _, ms in tmr.results()]))
+    tmr.close()
+    # the whole 1024-step loop as one graph; every replay must reproduce the eager run
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        h.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    replays = []
+    for _ in range(3):
+        h.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        replays.append(bool(torch.equal(ys, y_ref) and torch.equal(h, h_ref)))
+    graph_ms = timed(graph.replay, max(1, min(args.steps, 5)))
+    if not all(replays) or not (torch.equal(ys, y_ref) and torch.equal(h, h_ref)):
+        raise SystemExit("graph replay differs from the eager decode loop")
+    elems = B * D * N * L
+    per_step = B * D * N * 4 * 2 + 4 * B * D * 4 + 2 * B * N * 4 + 4 * D * (N + 2)
+    gbps = per_step / (kernel_ms * 1e-3) / 1e9
+    line = {
+        "metric": "selective-scan decode elements(B\u00b7D\u00b7N per token)/s and achieved HBM GB/s",
+        "value": elems / (eager_ms * 1e-3), "unit": "elements/s", "n_gpus": 1, "steps": L, "warmup": 1,
+        "ms_per_step": round(eager_ms / L, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{name}: batch={B} d_inner={D} d_state={N}, {L} consecutive steps from a zero "
+                               f"state, f32 (bf16-representable values)", "batch": B, "steps": L,
+                   "d_inner": D, "d_state": N, "io_dtype": "f32"},
+        "total_ms": {"eager": round(eager_ms, 3), "graph": round(graph_ms, 3)},
+        "graph": {"value": elems / (graph_ms * 1e-3), "replays_bitwise_equal_eager": replays},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_step",
+                     "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes_per_launch": per_step},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 8
+        hs = np.zeros((rows, D, N))
+        t0 = time.perf_counter()
+        steps = 0
+        while steps < L and time.perf_counter() - t0 < 20.0:
+            sl = {k: tm[k][steps, :rows].cpu().numpy() for k in ("x", "z", "dt", "B", "C")}
+            oracle.step(hs, sl["x"], sl["dt"], sl["B"], sl["C"], sl["z"], inp["A_log"], inp["D"], inp["dt_bias"])
+            steps += 1
+        sec = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": rows * D * N * steps / sec, "unit": "elements/s",
+                                "cores": oracle.num_threads(), "kind": "oracle",
+                                "sample": f"batch rows 0..{rows - 1}, all {D} channels, the first {steps} steps "
+                                          f"of the same workload in f64 ({sec:.1f} s, host copies included)"}
+    out = json.dumps(line)
+    print(out, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(out + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -234,6 +352,9 @@ def main():
         sys.exit(2)
     if args.op == "conv1d":
         conv_bench(args)
+        return
+    if args.op == "decode":
+        decode_bench(args)
         return
 
     import numpy as np

@@ -182,3 +182,12 @@ def test_bf16_outputs_are_nearest_even_roundings_of_the_f32_path():
     # parameter gradients are f32 sums of the same per-token products
     assert torch.equal(g16["dw"], g32["dw"])
     assert torch.equal(g16["dbias"], g32["dbias"])
+
+
+def test_long_sequence_and_max_batch():
+    """2^20 tokens (4096 blocks of 256 tokens in the partial sums) and, separately,
+    batch 65535 with a sequence shorter than the kernel width."""
+    inp = W.make_conv_inputs(1, 1 << 20, 12, 4, seed=41, with_ring=True)
+    _check(inp, torch.float32, F32_FWD, F32_GRAD)
+    inp = W.make_conv_inputs(65535, 2, 4, 4, seed=42, with_ring=True)
+    _check(inp, torch.float32, F32_FWD, F32_GRAD)

@@ -354,3 +354,22 @@ def test_bf16_outputs_are_nearest_even_roundings_of_the_f32_path():
         assert torch.equal(g16[k], g32[k].to(torch.bfloat16)), k
     for k in ("dA_log", "dD", "ddt_bias"):
         assert torch.equal(g16[k], g32[k]), k
+
+
+def test_max_chunk_count_long_sequence():
+    """2^18 tokens on 64 channels: the chunk planner reaches its largest chunk
+    counts (thousands of chunks in both directions), with slow decay so that
+    every carry is visible in the outputs."""
+    inp = W.make_inputs(1, 1 << 18, 64, dt_bias=W.DT_BIAS_SLOW, a_log=W.a_log_canonical(64, 16, shift=-4.0),
+                        seed=31)
+    _check_all(inp, want_dh0=True)
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_max_batch(io):
+    """batch 65535 (the largest grid dimension the launches use) on a short
+    sequence and few channels."""
+    bf = io == torch.bfloat16
+    inp = W.make_inputs(65535, 3, 4, seed=32, bf16=bf)
+    tol = (BF16_TOL, BF16_TOL) if bf else (F32_FWD, F32_GRAD)
+    _check_all(inp, io=io, fwd_tol=tol[0], grad_tol=tol[1], want_dh0=True)
