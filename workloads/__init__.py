@@ -138,3 +138,51 @@ def make_conv_config(name, *, seed=0):
     c = CONV_CONFIGS[name]
     return make_conv_inputs(c["batch"], c["seqlen"], c["d_inner"], c["d_conv"], seed=seed,
                             bf16=c["io"] == "bf16", with_bias=False)
+
+
+# One Mamba block around the scan (Mamba-2.8B layer shapes): d_model 2560,
+# d_inner 5120, d_state 16, dt_rank ceil(d_model / 16) = 160, d_conv 4.
+BLOCK_CONFIGS = {
+    "block_mamba2p8b_bf16": dict(batch=4, seqlen=8192, d_model=2560, d_inner=5120, d_state=16, dt_rank=160,
+                                 d_conv=4, io="bf16"),
+}
+
+
+def make_block_inputs(batch, seqlen, d_model, d_inner, d_state=D_STATE, dt_rank=None, d_conv=4, *, seed=0,
+                      bf16=False):
+    """Inputs of one Mamba block.  Draw order from default_rng(seed), each
+    standard_normal(float32): X [batch, seqlen, d_model], W_in [2 d_inner, d_model],
+    conv_w [d_inner, d_conv], conv_b [d_inner], W_x [dt_rank + 2 d_state, d_inner],
+    W_dt [d_inner, dt_rank], W_out [d_model, d_inner], dY [batch, seqlen, d_model].
+    Weights are scaled by min(1/sqrt(fan_in), 0.5) (the canonical init's projection
+    scale; the conv's fan-in is d_conv), the conv bias is zero, A_log = ln(1..N),
+    D = 1 and dt_bias gives softplus = 0.01 (the canonical S6 init).  With bf16
+    the activations X, dY and the projection weights are rounded to bf16."""
+    if dt_rank is None:
+        dt_rank = -(-d_model // 16)
+    rng = np.random.default_rng(seed)
+
+    def w(shape, fan_in):
+        return rng.standard_normal(shape, dtype=np.float32) * np.float32(min(1.0 / math.sqrt(fan_in), 0.5))
+
+    X = rng.standard_normal((batch, seqlen, d_model), dtype=np.float32)
+    p = {"W_in": w((2 * d_inner, d_model), d_model), "conv_w": w((d_inner, d_conv), d_conv)}
+    p["conv_b"] = np.zeros(d_inner, np.float32)
+    p["W_x"] = w((dt_rank + 2 * d_state, d_inner), d_inner)
+    p["W_dt"] = w((d_inner, dt_rank), dt_rank)
+    p["W_out"] = w((d_model, d_inner), d_inner)
+    dY = rng.standard_normal((batch, seqlen, d_model), dtype=np.float32)
+    p["A_log"] = a_log_canonical(d_inner, d_state)
+    p["D"] = np.ones(d_inner, np.float32)
+    p["dt_bias"] = np.full(d_inner, DT_BIAS_SLOW, np.float32)
+    if bf16:
+        X, dY = round_bf16(X), round_bf16(dY)
+        for k in ("W_in", "W_x", "W_dt", "W_out"):
+            p[k] = round_bf16(p[k])
+    return X, p, dY
+
+
+def make_block_config(name, *, seed=0):
+    c = BLOCK_CONFIGS[name]
+    return make_block_inputs(c["batch"], c["seqlen"], c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"],
+                             c["d_conv"], seed=seed, bf16=c["io"] == "bf16")
