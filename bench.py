@@ -59,11 +59,12 @@ def parse():
     ap.add_argument("--cpu-sample-channels", type=int, default=0,
                     help="channels the oracle baseline runs on (0 = all)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
-    ap.add_argument("--op", choices=("scan", "conv1d", "decode"), default="scan",
+    ap.add_argument("--op", choices=("scan", "conv1d", "decode", "block"), default="scan",
                     help="scan: the selective scan fwd+bwd (default); conv1d: the causal depthwise "
                          "conv1d + SiLU fwd+bwd in front of it, on the same batch/seqlen/d_inner; "
                          "decode: 1024 single-token steps at batch 256 x d_inner 5120, eager and "
-                         "replayed from a captured HIP graph")
+                         "replayed from a captured HIP graph; block: one Mamba block (projections on "
+                         "rocBLAS around the conv and the scan) fwd+bwd at the 2.8B layer shape")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to calibrate "
                          "profiler FETCH_SIZE / WRITE_SIZE counters")
@@ -344,6 +345,101 @@ def decode_bench(args):
             f.write(out + "\n")
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def block_bench(args):
+    """One Mamba block, forward (training) + backward, 4 x 8192 tokens at d_model
+    2560, d_inner 5120, dt_rank 160, d_conv 4, bf16 activations and projection
+    weights."""
+    import numpy as np
+    import torch
+
+    import selective_state_space_04_amd as ssm
+    import workloads as W
+
+    name = "block_mamba2p8b_bf16"
+    cfg = W.BLOCK_CONFIGS[name]
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
+    X, p, dY = W.make_block_config(name)
+    io = torch.bfloat16
+    Xd, dYd = torch.from_numpy(X).to(dev).to(io), torch.from_numpy(dY).to(dev).to(io)
+    pd = {k: torch.from_numpy(v).to(dev).to(io if k in ("W_in", "W_x", "W_dt", "W_out") else torch.float32)
+          for k, v in p.items()}
+    ctx = ssm.BlockContext()
+    Y = torch.empty_like(Xd)
+    grads = {}
+
+    def step(timer=None):
+        _, saved = ssm.ssm_block_fwd(ctx, Xd, pd, Y=Y, timing=timer)
+        ssm.ssm_block_bwd(ctx, Xd, pd, saved, dYd, out=grads, timing=timer)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # this library's own kernels, timed per launch; the rest of the step is the GEMMs
+    timers = [ssm.LaunchTimer() for _ in range(min(args.steps, 5))]
+    for tm in timers:
+        step(tm)
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for tm in timers:
+        for kname, kms in tm.results():
+            per_kernel.setdefault(kname, []).append(kms)
+        tm.close()
+    kavg = {k: float(np.sum(v)) / len(timers) for k, v in per_kernel.items()}
+    own_ms = sum(kavg.values())
+    B, L, dm, di, R, N = cfg["batch"], cfg["seqlen"], cfg["d_model"], cfg["d_inner"], cfg["dt_rank"], cfg["d_state"]
+    T = B * L
+    P = R + 2 * N
+    fwd_macs = T * (2 * di * dm + P * di + di * R + dm * di)
+    gemm_flops = 2 * fwd_macs * 3  # forward, data gradients, weight gradients
+    gemm_ms = max(ms - own_ms, 1e-6)
+    tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    line = {
+        "metric": "Mamba block fwd+bwd tokens/s",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: batch={B} seqlen={L} d_model={dm} d_inner={di} d_state={N} "
+                               f"dt_rank={R} d_conv={cfg['d_conv']}, bf16 activations and projection weights, "
+                               f"f32 accumulation and scan state, fwd+bwd",
+                   "batch": B, "seqlen": L, "d_model": dm, "d_inner": di, "dt_rank": R},
+        "kernels_ms": {k: round(v, 4) for k, v in sorted(kavg.items())},
+        "gemm": {"ms": round(gemm_ms, 4), "flops": gemm_flops,
+                 "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "traffic": None, "kernel": "rocBLAS GEMMs (15 per step, aggregate)"}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle.block import block_bwd
+        Lp = 256
+        t0 = time.perf_counter()
+        block_bwd(np.ascontiguousarray(X[:1, :Lp]), p, np.ascontiguousarray(dY[:1, :Lp]))
+        sec = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": Lp / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
+                                "kind": "oracle",
+                                "sample": f"batch row 0, the first {Lp} tokens of the same workload, forward "
+                                          f"and backward in f64 ({sec:.1f} s)"}
+    ctx.close()
+    out = json.dumps(line)
+    print(out, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(out + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -355,6 +451,9 @@ def main():
         return
     if args.op == "decode":
         decode_bench(args)
+        return
+    if args.op == "block":
+        block_bench(args)
         return
 
     import numpy as np

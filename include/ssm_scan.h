@@ -113,7 +113,8 @@ enum {
     SSM_K_CONV_BWD = 12,     /* its adjoint: dx, ring gradient, dw/dbias partials */
     SSM_K_CONV_BWD_REDUCE = 13, /* fixed-order sum of dw/dbias partials */
     SSM_K_CONV_STEP = 14,    /* one token through the conv ring */
-    SSM_K_CONV_RING = 15     /* ring copies/fills when seqlen == 0 */
+    SSM_K_CONV_RING = 15,    /* ring copies/fills when seqlen == 0 */
+    SSM_K_BLOCK_BC = 16      /* x_proj's B/C columns split / joined (ssm_block.h) */
 };
 
 /* Name of a kernel id (for matching profiler output); "?" if unknown. */

@@ -355,6 +355,139 @@ def ssm_conv1d_step(ring, x, w, bias=None, *, y=None, stream=None, timing=None):
     return y
 
 
+# ---------------------------------------------------------------- Mamba block
+BLOCK_LIB_PATH = os.path.join(_HERE, "libssmblock.so")
+_block_lib = None
+BLOCK_PARAMS = ("W_in", "conv_w", "conv_b", "W_x", "W_dt", "dt_bias", "A_log", "D", "W_out")
+
+
+class BlockDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_model", ctypes.c_int64),
+                ("d_inner", ctypes.c_int64), ("d_state", ctypes.c_int64), ("dt_rank", ctypes.c_int64),
+                ("d_conv", ctypes.c_int64), ("io_dtype", ctypes.c_int32)]
+
+
+class BlockParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_PARAMS]
+
+
+class BlockGrads(ctypes.Structure):
+    _fields_ = [("d" + n, ctypes.c_void_p) for n in BLOCK_PARAMS]
+
+
+def block_library():
+    """libssmblock.so (the Mamba block: projections on rocBLAS around this
+    library's conv and scan kernels), loaded on first use."""
+    global _block_lib
+    if _block_lib is not None:
+        return _block_lib
+    if not os.path.exists(BLOCK_LIB_PATH):
+        raise ImportError(f"{BLOCK_LIB_PATH} is missing: build the HIP libraries first")
+    lib = ctypes.CDLL(BLOCK_LIB_PATH)
+    P, SZ = ctypes.c_void_p, ctypes.c_size_t
+    DP = ctypes.POINTER(BlockDims)
+    lib.ssm_block_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.ssm_block_create.restype = ctypes.c_int
+    lib.ssm_block_destroy.argtypes = [P]
+    lib.ssm_block_destroy.restype = None
+    for fn in ("ssm_block_saved_bytes", "ssm_block_fwd_workspace_bytes", "ssm_block_bwd_workspace_bytes"):
+        getattr(lib, fn).argtypes = [DP]
+        getattr(lib, fn).restype = SZ
+    lib.ssm_block_fwd.argtypes = [P, DP, P, ctypes.POINTER(BlockParams), P, P, P, SZ, P,
+                                  ctypes.POINTER(SsmTiming)]
+    lib.ssm_block_fwd.restype = ctypes.c_int
+    lib.ssm_block_bwd.argtypes = [P, DP, P, ctypes.POINTER(BlockParams), P, P, P, ctypes.POINTER(BlockGrads),
+                                  P, SZ, P, ctypes.POINTER(SsmTiming)]
+    lib.ssm_block_bwd.restype = ctypes.c_int
+    _block_lib = lib
+    return lib
+
+
+class BlockContext:
+    """A rocBLAS handle on the current device for ssm_block_fwd / ssm_block_bwd."""
+
+    def __init__(self):
+        self._lib = block_library()
+        self.ptr = ctypes.c_void_p()
+        _raise("ssm_block_create", self._lib.ssm_block_create(ctypes.byref(self.ptr)))
+
+    def close(self):
+        if self.ptr:
+            self._lib.ssm_block_destroy(self.ptr)
+            self.ptr = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _block_check(X, prm):
+    dev = X.device
+    bsz, L, dm = X.shape
+    io = X.dtype
+    di = prm["W_in"].shape[0] // 2
+    R = prm["W_dt"].shape[1]
+    N = prm["A_log"].shape[1]
+    K = prm["conv_w"].shape[1]
+    _check(X, "X", (bsz, L, dm), io, dev)
+    shapes = {"W_in": ((2 * di, dm), io), "conv_w": ((di, K), torch.float32), "W_x": ((R + 2 * N, di), io),
+              "W_dt": ((di, R), io), "dt_bias": ((di,), torch.float32), "A_log": ((di, N), torch.float32),
+              "D": ((di,), torch.float32), "W_out": ((dm, di), io)}
+    for n, (shp, dt) in shapes.items():
+        _check(prm.get(n), n, shp, dt, dev)
+    _check(prm.get("conv_b"), "conv_b", (di,), torch.float32, dev, required=False)
+    dm_ = BlockDims(bsz, L, dm, di, N, R, K, _io_code(io))
+    pp = BlockParams(*[None if prm.get(n) is None else prm[n].data_ptr() for n in BLOCK_PARAMS])
+    return dm_, pp, dev
+
+
+def ssm_block_fwd(ctx, X, params, *, training=True, Y=None, stream=None, timing=None):
+    """One Mamba block.  X [batch, L, d_model] (float32 or bfloat16); params: dict
+    with W_in [2 d_inner, d_model], W_x [dt_rank + 32, d_inner], W_dt [d_inner,
+    dt_rank], W_out [d_model, d_inner] (X's dtype) and conv_w [d_inner, d_conv],
+    conv_b [d_inner] (optional), dt_bias [d_inner], A_log [d_inner, 16], D [d_inner]
+    (float32).  Returns (Y, saved or None); ssm_block_bwd needs `saved`."""
+    lib = block_library()
+    dm, pp, dev = _block_check(X, params)
+    if Y is None:
+        Y = torch.empty_like(X)
+    _check(Y, "Y", tuple(X.shape), X.dtype, dev)
+    saved = None
+    if training:
+        saved = torch.empty(lib.ssm_block_saved_bytes(ctypes.byref(dm)), dtype=torch.uint8, device=dev)
+    nws = lib.ssm_block_fwd_workspace_bytes(ctypes.byref(dm))
+    ws = _workspace(nws, dev)
+    rc = lib.ssm_block_fwd(ctx.ptr, ctypes.byref(dm), _ptr(X), ctypes.byref(pp), _ptr(Y), _ptr(saved), _ptr(ws),
+                           nws, _stream(dev, stream), _timing_ptr(timing))
+    _raise("ssm_block_fwd", rc)
+    return Y, saved
+
+
+def ssm_block_bwd(ctx, X, params, saved, dY, *, out=None, stream=None, timing=None):
+    """Backward of ssm_block_fwd for the loss sum(dY * Y).  Returns a dict with dX
+    (X's dtype) and d<name> (float32, summed over batch and time) for every
+    parameter."""
+    lib = block_library()
+    dm, pp, dev = _block_check(X, params)
+    _check(dY, "dY", tuple(X.shape), X.dtype, dev)
+    _check(saved, "saved", (lib.ssm_block_saved_bytes(ctypes.byref(dm)),), torch.uint8, dev)
+    g = out if out is not None else {}
+    g.setdefault("dX", torch.empty_like(X))
+    for n in BLOCK_PARAMS:
+        ref = params[n] if params.get(n) is not None else params["D"]
+        g.setdefault("d" + n, torch.empty(ref.shape, dtype=torch.float32, device=dev))
+    gg = BlockGrads(*[g["d" + n].data_ptr() for n in BLOCK_PARAMS])
+    nws = lib.ssm_block_bwd_workspace_bytes(ctypes.byref(dm))
+    ws = _workspace(nws, dev)
+    rc = lib.ssm_block_bwd(ctx.ptr, ctypes.byref(dm), _ptr(X), ctypes.byref(pp), _ptr(saved), _ptr(dY),
+                           _ptr(g["dX"]), ctypes.byref(gg), _ptr(ws), nws, _stream(dev, stream),
+                           _timing_ptr(timing))
+    _raise("ssm_block_bwd", rc)
+    return g
+
+
 class LaunchTimer:
     """Per-kernel timing through the ABI's optional launch log: HIP events recorded
     by the library around each of its launches, on the launch stream."""
@@ -406,4 +539,5 @@ class LaunchTimer:
 __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_scan_step", "ckpt_bytes", "fwd_workspace_bytes",
            "bwd_workspace_bytes", "LaunchTimer", "SsmError", "library", "status_str", "kernel_name",
            "SsmDims", "SsmTiming", "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_conv1d_step",
-           "conv1d_bwd_workspace_bytes", "ConvDims"]
+           "conv1d_bwd_workspace_bytes", "ConvDims", "BlockContext", "ssm_block_fwd", "ssm_block_bwd",
+           "block_library", "BlockDims"]

@@ -1,5 +1,6 @@
 """Compiles libssmscan.so (HIP, gfx950 only: the selective scan and the conv1d
-in front of it) in-tree with hipcc."""
+in front of it) and libssmblock.so (one Mamba block: those kernels plus the
+projections on rocBLAS) in-tree with hipcc."""
 import os
 import subprocess
 
@@ -8,6 +9,9 @@ ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", "ssm_scan.hip"), os.path.join(HERE, "csrc", "ssm_conv1d.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libssmscan.so")
+BLOCK_SRC = os.path.join(HERE, "csrc", "ssm_block.hip")
+BLOCK_LIB_PATH = os.path.join(HERE, "libssmblock.so")
+ROCM_LIB = "/opt/rocm/lib"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -19,9 +23,9 @@ FLAGS = [
 ]
 
 
-def build(verbose=False, extra=()):
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, *SRCS, "-o", tmp]
+def _hipcc(cmd, out, verbose):
+    tmp = out + ".tmp"
+    cmd = cmd + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -31,5 +35,14 @@ def build(verbose=False, extra=()):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+
+
+def build(verbose=False, extra=()):
+    """libssmscan.so (scan + conv1d kernels), then libssmblock.so (the Mamba block
+    on top of it and rocBLAS)."""
+    _hipcc([HIPCC, *FLAGS, *extra, "-I", INCLUDE, *SRCS], LIB_PATH, verbose)
+    _hipcc([HIPCC, *FLAGS, *extra, "-I", INCLUDE, BLOCK_SRC, "-L", HERE, "-lssmscan",
+            f"-L{ROCM_LIB}", "-lrocblas", "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{ROCM_LIB}"],
+           BLOCK_LIB_PATH, verbose)
     return LIB_PATH

@@ -1,0 +1,361 @@
+// ssm_block.hip -- one Mamba block around the selective scan, on one MI355X:
+// the four projections on rocBLAS (bf16 or f32 operands, f32 accumulation), the
+// conv1d + SiLU and the scan on this project's kernels, everything on the
+// caller's stream.  Built as libssmblock.so on top of libssmscan.so.
+//
+// Operation (rustytorch commit log, page "crates/training/rtx-transformers/tests":
+// the real-S6-forward commit and the hand-written VJP commit):
+//   xi = X W_in[:di]^T, z = X W_in[di:]^T, xc = silu(conv1d(xi)),
+//   (dt_low, B, C) = xc W_x^T, dt = dt_low W_dt^T,
+//   y_s = scan(xc, dt, B, C, z; A_log, D, dt_bias), Y = y_s W_out^T,
+// and the chain rule back through the same steps.
+//
+// Activations are token-major [T, features] (T = batch*seqlen), the layout the
+// conv and scan kernels read, so every projection is one row-major GEMM with
+// no transposes of data; x_proj's B and C columns are split into the dense
+// [T, 16] arrays the scan takes (and joined back for the backward) by a small
+// copy kernel.
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "ssm_block.h"
+#include "ssm_common.h"
+#include "ssm_conv1d.h"
+#include "ssm_scan.h"
+
+struct ssm_block_ctx {
+    rocblas_handle h;
+};
+
+namespace {
+
+using ssm::bf16_t;
+using ssm::misaligned;
+
+constexpr int WG = 256;
+constexpr int NS = 16;
+
+struct Plan {
+    int64_t Bt, L, T, dm, di, N, R, K, P;
+    int io;
+    size_t esz;
+};
+
+ssm_status check_block(const ssm_block_dims* d) {
+    if (!d) return SSM_E_NULLPTR;
+    if (d->batch < 1 || d->seqlen < 1 || d->d_model < 1 || d->d_inner < 1 || d->d_state < 1 ||
+        d->dt_rank < 1 || d->d_conv < 1)
+        return SSM_E_SHAPE;
+    if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_E_DTYPE;
+    if (d->d_model % 8 || d->d_inner % 8) return SSM_E_SHAPE;  // 16-byte rows for every operand
+    if (d->d_state != NS || d->d_conv > 4 || d->batch > 65535) return SSM_E_UNSUPPORTED;
+    if (d->batch * d->seqlen >= ((int64_t)1 << 31) || d->d_inner >= ((int64_t)1 << 28) ||
+        d->d_model >= ((int64_t)1 << 28) || d->dt_rank >= ((int64_t)1 << 20))
+        return SSM_E_UNSUPPORTED;
+    return SSM_OK;
+}
+
+Plan make_plan(const ssm_block_dims* d) {
+    Plan p;
+    p.Bt = d->batch;
+    p.L = d->seqlen;
+    p.T = p.Bt * p.L;
+    p.dm = d->d_model;
+    p.di = d->d_inner;
+    p.N = d->d_state;
+    p.R = d->dt_rank;
+    p.K = d->d_conv;
+    p.P = p.R + 2 * p.N;
+    p.io = d->io_dtype;
+    p.esz = p.io == SSM_BF16 ? 2 : 4;
+    return p;
+}
+
+ssm_dims scan_dims(const Plan& p) { return ssm_dims{p.Bt, p.L, p.di, p.N, p.io}; }
+ssm_conv_dims conv_dims(const Plan& p) { return ssm_conv_dims{p.Bt, p.L, p.di, p.K, p.io}; }
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Sequential 256-byte aligned carve-up of a buffer.
+struct Carve {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    }
+};
+
+// Activations the backward needs (the forward's intermediates and the scan's
+// checkpoints).
+struct Saved {
+    size_t xi, z, xc, proj, Bm, Cm, dt, ys, ckpt, total;
+};
+Saved saved_layout(const Plan& p) {
+    Carve c;
+    Saved s;
+    const size_t act = (size_t)p.T * p.di * p.esz;
+    s.xi = c.take(act);
+    s.z = c.take(act);
+    s.xc = c.take(act);
+    s.proj = c.take((size_t)p.T * p.P * p.esz);
+    s.Bm = c.take((size_t)p.T * p.N * p.esz);
+    s.Cm = c.take((size_t)p.T * p.N * p.esz);
+    s.dt = c.take(act);
+    s.ys = c.take(act);
+    const ssm_dims sd = scan_dims(p);
+    s.ckpt = c.take(ssm_scan_ckpt_bytes(&sd));
+    s.total = c.off;
+    return s;
+}
+
+// Forward workspace: the intermediates (used when no `saved` buffer is given)
+// and the scan's own workspace.
+struct FwdWs {
+    size_t act, scan, total;
+};
+FwdWs fwd_ws(const Plan& p) {
+    Carve c;
+    FwdWs w;
+    const Saved s = saved_layout(p);
+    w.act = c.take(s.ckpt);  // everything before the checkpoints
+    const ssm_dims sd = scan_dims(p);
+    w.scan = c.take(ssm_scan_fwd_workspace_bytes(&sd));
+    w.total = c.off;
+    return w;
+}
+
+struct BwdWs {
+    size_t dys, dxc, ddt, dB, dC, dz, dproj, dxi, conv, scan, total;
+};
+BwdWs bwd_ws(const Plan& p) {
+    Carve c;
+    BwdWs w;
+    const size_t act = (size_t)p.T * p.di * p.esz;
+    w.dys = c.take(act);
+    w.dxc = c.take(act);
+    w.ddt = c.take(act);
+    w.dB = c.take((size_t)p.T * p.N * p.esz);
+    w.dC = c.take((size_t)p.T * p.N * p.esz);
+    w.dz = c.take(act);
+    w.dproj = c.take((size_t)p.T * p.P * p.esz);
+    w.dxi = c.take(act);
+    const ssm_conv_dims cd = conv_dims(p);
+    w.conv = c.take(ssm_conv1d_bwd_workspace_bytes(&cd));
+    const ssm_dims sd = scan_dims(p);
+    w.scan = c.take(ssm_scan_bwd_workspace_bytes(&sd));
+    w.total = c.off;
+    return w;
+}
+
+// ------------------------------------------------------------------ GEMMs
+// Row-major C[m, n] (ldc) = opA(A) opB(B) + beta C, where opA(A) = A [m, k] (lda)
+// or, with ta, A^T for A stored [k, m]; opB(B) = B [k, n] (ldb) or, with tb, B^T
+// for B stored [n, k].  rocBLAS is column-major, so this is the column-major
+// product C^T = opB(B)^T opA(A)^T with the operands swapped.
+struct Gemm {
+    rocblas_handle h;
+    rocblas_datatype ab, io_c;
+    ssm_status operator()(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
+                          const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
+                          bool f32_out = false) const {
+        const float alpha = 1.0f;
+        const rocblas_datatype ct = f32_out ? rocblas_datatype_f32_r : io_c;
+        const rocblas_status st = rocblas_gemm_ex(
+            h, tb ? rocblas_operation_transpose : rocblas_operation_none,
+            ta ? rocblas_operation_transpose : rocblas_operation_none, (rocblas_int)n, (rocblas_int)m,
+            (rocblas_int)k, &alpha, B, ab, (rocblas_int)ldb, A, ab, (rocblas_int)lda, &beta, C, ct,
+            (rocblas_int)ldc, C, ct, (rocblas_int)ldc, rocblas_datatype_f32_r, rocblas_gemm_algo_standard,
+            0, 0);
+        return st == rocblas_status_success ? SSM_OK : SSM_E_LAUNCH;
+    }
+};
+
+// ------------------------------------------------------------------ B/C columns
+// proj [T, R + 2N] -> B, C [T, N] (forward) and back (backward, into dproj).
+template <typename T>
+__global__ __launch_bounds__(WG) void k_split_bc(const T* __restrict__ proj, T* __restrict__ Bm,
+                                                 T* __restrict__ Cm, int64_t n, int R, int N) {
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (i >= n) return;
+    const int64_t t = i / (2 * N);
+    const int j = (int)(i % (2 * N));
+    const T v = proj[t * (R + 2 * N) + R + j];
+    if (j < N) Bm[t * N + j] = v;
+    else Cm[t * N + (j - N)] = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(WG) void k_join_bc(const T* __restrict__ dB, const T* __restrict__ dC,
+                                                T* __restrict__ dproj, int64_t n, int R, int N) {
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (i >= n) return;
+    const int64_t t = i / (2 * N);
+    const int j = (int)(i % (2 * N));
+    dproj[t * (R + 2 * N) + R + j] = j < N ? dB[t * N + j] : dC[t * N + (j - N)];
+}
+
+ssm_status launch_bc(const Plan& p, bool split, const void* a, const void* b, void* c, hipStream_t s,
+                     ssm_timing* tm) {
+    ssm::Launcher launch{s, tm};
+    const int64_t n = p.T * 2 * p.N;
+    const dim3 grid((unsigned)((n + WG - 1) / WG));
+    if (p.io == SSM_F32) {
+        return split ? launch(SSM_K_BLOCK_BC, k_split_bc<float>, grid, dim3(WG), (const float*)a, (float*)b,
+                              (float*)c, n, (int)p.R, (int)p.N)
+                     : launch(SSM_K_BLOCK_BC, k_join_bc<float>, grid, dim3(WG), (const float*)a, (const float*)b,
+                              (float*)c, n, (int)p.R, (int)p.N);
+    }
+    return split ? launch(SSM_K_BLOCK_BC, k_split_bc<bf16_t>, grid, dim3(WG), (const bf16_t*)a, (bf16_t*)b,
+                          (bf16_t*)c, n, (int)p.R, (int)p.N)
+                 : launch(SSM_K_BLOCK_BC, k_join_bc<bf16_t>, grid, dim3(WG), (const bf16_t*)a, (const bf16_t*)b,
+                          (bf16_t*)c, n, (int)p.R, (int)p.N);
+}
+
+bool any_misaligned(std::initializer_list<const void*> ptrs) {
+    for (const void* q : ptrs)
+        if (q && misaligned(q)) return true;
+    return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_block_create(ssm_block_ctx** ctx) {
+    if (!ctx) return SSM_E_NULLPTR;
+    *ctx = nullptr;
+    rocblas_handle h;
+    if (rocblas_create_handle(&h) != rocblas_status_success) return SSM_E_LAUNCH;
+    // no atomics inside GEMMs: repeated calls give bitwise identical results
+    if (rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed) != rocblas_status_success) {
+        rocblas_destroy_handle(h);
+        return SSM_E_LAUNCH;
+    }
+    *ctx = new ssm_block_ctx{h};
+    return SSM_OK;
+}
+
+void ssm_block_destroy(ssm_block_ctx* ctx) {
+    if (!ctx) return;
+    rocblas_destroy_handle(ctx->h);
+    delete ctx;
+}
+
+size_t ssm_block_saved_bytes(const ssm_block_dims* dims) {
+    if (check_block(dims) != SSM_OK) return 0;
+    return saved_layout(make_plan(dims)).total;
+}
+
+size_t ssm_block_fwd_workspace_bytes(const ssm_block_dims* dims) {
+    if (check_block(dims) != SSM_OK) return 0;
+    return fwd_ws(make_plan(dims)).total;
+}
+
+size_t ssm_block_bwd_workspace_bytes(const ssm_block_dims* dims) {
+    if (check_block(dims) != SSM_OK) return 0;
+    return bwd_ws(make_plan(dims)).total;
+}
+
+ssm_status ssm_block_fwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const void* X,
+                         const ssm_block_params* p, void* Y, void* saved, void* ws, size_t ws_bytes,
+                         hipStream_t stream, ssm_timing* timing) {
+    if (!ctx || !p) return SSM_E_NULLPTR;
+    SSM_TRY(check_block(dims));
+    const Plan q = make_plan(dims);
+    if (!X || !Y || !p->W_in || !p->conv_w || !p->W_x || !p->W_dt || !p->dt_bias || !p->A_log || !p->D ||
+        !p->W_out)
+        return SSM_E_NULLPTR;
+    if (any_misaligned({X, Y, saved, ws, p->W_in, p->conv_w, p->conv_b, p->W_x, p->W_dt, p->dt_bias, p->A_log,
+                        p->D, p->W_out}))
+        return SSM_E_ALIGN;
+    const FwdWs w = fwd_ws(q);
+    if (!ws || ws_bytes < w.total) return SSM_E_WORKSPACE;
+    (void)hipGetLastError();
+    if (rocblas_set_stream(ctx->h, stream) != rocblas_status_success) return SSM_E_LAUNCH;
+    const Saved s = saved_layout(q);
+    char* act = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + w.act;
+    void *xi = act + s.xi, *z = act + s.z, *xc = act + s.xc, *proj = act + s.proj, *Bm = act + s.Bm,
+         *Cm = act + s.Cm, *dt = act + s.dt, *ys = act + s.ys;
+    float* ckpt = saved ? reinterpret_cast<float*>(act + s.ckpt) : nullptr;
+    const rocblas_datatype io_t = q.io == SSM_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+    const Gemm gemm{ctx->h, io_t, io_t};
+    const char* W_in = static_cast<const char*>(p->W_in);
+    const size_t half = (size_t)q.di * q.dm * q.esz;
+    SSM_TRY(gemm(false, true, q.T, q.di, q.dm, X, q.dm, W_in, q.dm, 0.0f, xi, q.di));
+    SSM_TRY(gemm(false, true, q.T, q.di, q.dm, X, q.dm, W_in + half, q.dm, 0.0f, z, q.di));
+    const ssm_conv_dims cd = conv_dims(q);
+    SSM_TRY(ssm_conv1d_fwd(&cd, xi, p->conv_w, p->conv_b, nullptr, xc, nullptr, stream, timing));
+    SSM_TRY(gemm(false, true, q.T, q.P, q.di, xc, q.di, p->W_x, q.di, 0.0f, proj, q.P));
+    SSM_TRY(launch_bc(q, true, proj, Bm, Cm, stream, timing));
+    SSM_TRY(gemm(false, true, q.T, q.di, q.R, proj, q.P, p->W_dt, q.R, 0.0f, dt, q.di));
+    const ssm_dims sd = scan_dims(q);
+    SSM_TRY(ssm_scan_fwd(&sd, xc, dt, Bm, Cm, z, p->A_log, p->D, p->dt_bias, nullptr, ys, nullptr, ckpt,
+                         static_cast<char*>(ws) + w.scan, w.total - w.scan, stream, timing));
+    return gemm(false, true, q.T, q.dm, q.di, ys, q.di, p->W_out, q.di, 0.0f, Y, q.dm);
+}
+
+ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const void* X,
+                         const ssm_block_params* p, const void* saved, const void* dY, void* dX,
+                         const ssm_block_grads* g, void* ws, size_t ws_bytes, hipStream_t stream,
+                         ssm_timing* timing) {
+    if (!ctx || !p || !g) return SSM_E_NULLPTR;
+    SSM_TRY(check_block(dims));
+    const Plan q = make_plan(dims);
+    if (!X || !saved || !dY || !dX || !p->W_in || !p->conv_w || !p->W_x || !p->W_dt || !p->dt_bias ||
+        !p->A_log || !p->D || !p->W_out)
+        return SSM_E_NULLPTR;
+    if (!g->dW_in || !g->dconv_w || !g->dconv_b || !g->dW_x || !g->dW_dt || !g->ddt_bias || !g->dA_log ||
+        !g->dD || !g->dW_out)
+        return SSM_E_NULLPTR;
+    if (any_misaligned({X, saved, dY, dX, ws, p->W_in, p->conv_w, p->conv_b, p->W_x, p->W_dt, p->dt_bias,
+                        p->A_log, p->D, p->W_out, g->dW_in, g->dconv_w, g->dconv_b, g->dW_x, g->dW_dt,
+                        g->ddt_bias, g->dA_log, g->dD, g->dW_out}))
+        return SSM_E_ALIGN;
+    const BwdWs w = bwd_ws(q);
+    if (!ws || ws_bytes < w.total) return SSM_E_WORKSPACE;
+    (void)hipGetLastError();
+    if (rocblas_set_stream(ctx->h, stream) != rocblas_status_success) return SSM_E_LAUNCH;
+    const Saved s = saved_layout(q);
+    const char* act = static_cast<const char*>(saved);
+    const void *xi = act + s.xi, *z = act + s.z, *xc = act + s.xc, *proj = act + s.proj, *Bm = act + s.Bm,
+               *Cm = act + s.Cm, *dt = act + s.dt, *ys = act + s.ys;
+    const float* ckpt = reinterpret_cast<const float*>(act + s.ckpt);
+    char* wb = static_cast<char*>(ws);
+    void *dys = wb + w.dys, *dxc = wb + w.dxc, *ddt = wb + w.ddt, *dB = wb + w.dB, *dC = wb + w.dC,
+         *dz = wb + w.dz, *dproj = wb + w.dproj, *dxi = wb + w.dxi;
+    const rocblas_datatype io_t = q.io == SSM_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+    const Gemm gemm{ctx->h, io_t, io_t};
+    // out_proj
+    SSM_TRY(gemm(false, false, q.T, q.di, q.dm, dY, q.dm, p->W_out, q.di, 0.0f, dys, q.di));
+    SSM_TRY(gemm(true, false, q.dm, q.di, q.T, dY, q.dm, ys, q.di, 0.0f, g->dW_out, q.di, true));
+    // scan
+    const ssm_dims sd = scan_dims(q);
+    SSM_TRY(ssm_scan_bwd(&sd, xc, dt, Bm, Cm, z, p->A_log, p->D, p->dt_bias, nullptr, ckpt, dys, dxc, ddt, dB,
+                         dC, dz, g->dA_log, g->dD, g->ddt_bias, nullptr, wb + w.scan, w.total - w.scan, stream,
+                         timing));
+    // dt_proj: d dt_low lands in the first R columns of dproj; x_proj's B/C columns follow
+    SSM_TRY(gemm(false, false, q.T, q.R, q.di, ddt, q.di, p->W_dt, q.R, 0.0f, dproj, q.P));
+    SSM_TRY(gemm(true, false, q.di, q.R, q.T, ddt, q.di, proj, q.P, 0.0f, g->dW_dt, q.R, true));
+    SSM_TRY(launch_bc(q, false, dB, dC, dproj, stream, timing));
+    // x_proj: dxc += dproj W_x
+    SSM_TRY(gemm(false, false, q.T, q.di, q.P, dproj, q.P, p->W_x, q.di, 1.0f, dxc, q.di));
+    SSM_TRY(gemm(true, false, q.P, q.di, q.T, dproj, q.P, xc, q.di, 0.0f, g->dW_x, q.di, true));
+    // conv1d + SiLU
+    const ssm_conv_dims cd = conv_dims(q);
+    SSM_TRY(ssm_conv1d_bwd(&cd, xi, p->conv_w, p->conv_b, nullptr, dxc, dxi, g->dconv_w, g->dconv_b, nullptr,
+                           wb + w.conv, w.scan - w.conv, stream, timing));
+    // in_proj
+    const char* W_in = static_cast<const char*>(p->W_in);
+    const size_t half = (size_t)q.di * q.dm * q.esz;
+    SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dxi, q.di, W_in, q.dm, 0.0f, dX, q.dm));
+    SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dz, q.di, W_in + half, q.dm, 1.0f, dX, q.dm));
+    SSM_TRY(gemm(true, false, q.di, q.dm, q.T, dxi, q.di, X, q.dm, 0.0f, g->dW_in, q.dm, true));
+    return gemm(true, false, q.di, q.dm, q.T, dz, q.di, X, q.dm, 0.0f, g->dW_in + (size_t)q.di * q.dm, q.dm,
+                true);
+}
+
+}  // extern "C"

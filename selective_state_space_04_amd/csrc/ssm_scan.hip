@@ -959,6 +959,7 @@ const char* ssm_kernel_name(int32_t id) {
         case SSM_K_CONV_BWD_REDUCE: return "k_conv_bwd_reduce";
         case SSM_K_CONV_STEP: return "k_conv_step";
         case SSM_K_CONV_RING: return "k_conv_ring";
+        case SSM_K_BLOCK_BC: return "k_block_bc";
     }
     return "?";
 }
