@@ -19,6 +19,7 @@
 #include <rocblas/rocblas.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <initializer_list>
 
 #include "ssm_block.h"
@@ -128,8 +129,19 @@ FwdWs fwd_ws(const Plan& p) {
     return w;
 }
 
+// Weight gradients sum over all T tokens (the GEMM's K).  Their outputs are
+// small next to K, so one GEMM has few output tiles for 256 CUs; the tokens are
+// split into S equal chunks computed as one strided-batched GEMM into f32
+// partials, which a fixed-order kernel then sums (deterministic).
+int64_t wgrad_splits(int64_t m, int64_t n, int64_t T) {
+    const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
+    int64_t S = 1;
+    while (S < 16 && tiles * S < 512 && T % (2 * S) == 0 && T / (2 * S) >= 2048) S *= 2;
+    return S;
+}
+
 struct BwdWs {
-    size_t dys, dxc, ddt, dB, dC, dz, dproj, dxi, conv, scan, total;
+    size_t dys, dxc, ddt, dB, dC, dz, dproj, dxi, conv, scan, part, total;
 };
 BwdWs bwd_ws(const Plan& p) {
     Carve c;
@@ -147,6 +159,14 @@ BwdWs bwd_ws(const Plan& p) {
     w.conv = c.take(ssm_conv1d_bwd_workspace_bytes(&cd));
     const ssm_dims sd = scan_dims(p);
     w.scan = c.take(ssm_scan_bwd_workspace_bytes(&sd));
+    // partials of the largest split weight gradient (in_proj halves, out_proj, x_proj, dt_proj)
+    size_t part = 0;
+    const int64_t shapes[4][2] = {{p.di, p.dm}, {p.dm, p.di}, {p.P, p.di}, {p.di, p.R}};
+    for (const auto& mn : shapes) {
+        const int64_t S = wgrad_splits(mn[0], mn[1], p.T);
+        if (S > 1) part = std::max(part, sizeof(float) * (size_t)(S * mn[0] * mn[1]));
+    }
+    w.part = c.take(part);
     w.total = c.off;
     return w;
 }
@@ -173,6 +193,39 @@ struct Gemm {
         return st == rocblas_status_success ? SSM_OK : SSM_E_LAUNCH;
     }
 };
+
+// C[i] = sum_s part[s][i], s in increasing order.
+__global__ __launch_bounds__(WG) void k_sum_parts(const float* __restrict__ part, float* __restrict__ C,
+                                                  int64_t mn, int S) {
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (i >= mn) return;
+    float acc = part[i];
+    for (int s = 1; s < S; ++s) acc += part[(int64_t)s * mn + i];
+    C[i] = acc;
+}
+
+// Row-major f32 weight gradient C[m, n] = A^T B over T tokens, A [T, m] (lda),
+// B [T, n] (ldb), with the tokens split as described at wgrad_splits.
+ssm_status wgrad(const Gemm& g, int64_t m, int64_t n, int64_t T, const void* A, int64_t lda, const void* B,
+                 int64_t ldb, float* C, float* part, size_t esz, hipStream_t s, ssm_timing* tm) {
+    const int64_t S = wgrad_splits(m, n, T);
+    if (S == 1) return g(true, false, m, n, T, A, lda, B, ldb, 0.0f, C, n, true);
+    const int64_t Tc = T / S;
+    const float alpha = 1.0f, beta = 0.0f;
+    // column-major view as in Gemm: C^T [n, m] = B^T [n, Tc] . A [Tc, m] per chunk
+    const rocblas_status st = rocblas_gemm_strided_batched_ex(
+        g.h, rocblas_operation_none, rocblas_operation_transpose, (rocblas_int)n, (rocblas_int)m,
+        (rocblas_int)Tc, &alpha, B, g.ab, (rocblas_int)ldb, (rocblas_stride)(Tc * ldb), A, g.ab,
+        (rocblas_int)lda, (rocblas_stride)(Tc * lda), &beta, part, rocblas_datatype_f32_r, (rocblas_int)n,
+        (rocblas_stride)(m * n), part, rocblas_datatype_f32_r, (rocblas_int)n, (rocblas_stride)(m * n),
+        (rocblas_int)S, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+    (void)esz;
+    if (st != rocblas_status_success) return SSM_E_LAUNCH;
+    ssm::Launcher launch{s, tm};
+    const int64_t mn = m * n;
+    return launch(SSM_K_BLOCK_BC, k_sum_parts, dim3((unsigned)((mn + WG - 1) / WG)), dim3(WG),
+                  (const float*)part, C, mn, (int)S);
+}
 
 // ------------------------------------------------------------------ B/C columns
 // proj [T, R + 2N] -> B, C [T, N] (forward) and back (backward, into dproj).
@@ -331,7 +384,8 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     const Gemm gemm{ctx->h, io_t, io_t};
     // out_proj
     SSM_TRY(gemm(false, false, q.T, q.di, q.dm, dY, q.dm, p->W_out, q.di, 0.0f, dys, q.di));
-    SSM_TRY(gemm(true, false, q.dm, q.di, q.T, dY, q.dm, ys, q.di, 0.0f, g->dW_out, q.di, true));
+    float* part = reinterpret_cast<float*>(wb + w.part);
+    SSM_TRY(wgrad(gemm, q.dm, q.di, q.T, dY, q.dm, ys, q.di, g->dW_out, part, q.esz, stream, timing));
     // scan
     const ssm_dims sd = scan_dims(q);
     SSM_TRY(ssm_scan_bwd(&sd, xc, dt, Bm, Cm, z, p->A_log, p->D, p->dt_bias, nullptr, ckpt, dys, dxc, ddt, dB,
@@ -339,11 +393,11 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
                          timing));
     // dt_proj: d dt_low lands in the first R columns of dproj; x_proj's B/C columns follow
     SSM_TRY(gemm(false, false, q.T, q.R, q.di, ddt, q.di, p->W_dt, q.R, 0.0f, dproj, q.P));
-    SSM_TRY(gemm(true, false, q.di, q.R, q.T, ddt, q.di, proj, q.P, 0.0f, g->dW_dt, q.R, true));
+    SSM_TRY(wgrad(gemm, q.di, q.R, q.T, ddt, q.di, proj, q.P, g->dW_dt, part, q.esz, stream, timing));
     SSM_TRY(launch_bc(q, false, dB, dC, dproj, stream, timing));
     // x_proj: dxc += dproj W_x
     SSM_TRY(gemm(false, false, q.T, q.di, q.P, dproj, q.P, p->W_x, q.di, 1.0f, dxc, q.di));
-    SSM_TRY(gemm(true, false, q.P, q.di, q.T, dproj, q.P, xc, q.di, 0.0f, g->dW_x, q.di, true));
+    SSM_TRY(wgrad(gemm, q.P, q.di, q.T, dproj, q.P, xc, q.di, g->dW_x, part, q.esz, stream, timing));
     // conv1d + SiLU
     const ssm_conv_dims cd = conv_dims(q);
     SSM_TRY(ssm_conv1d_bwd(&cd, xi, p->conv_w, p->conv_b, nullptr, dxc, dxi, g->dconv_w, g->dconv_b, nullptr,
@@ -353,9 +407,9 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     const size_t half = (size_t)q.di * q.dm * q.esz;
     SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dxi, q.di, W_in, q.dm, 0.0f, dX, q.dm));
     SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dz, q.di, W_in + half, q.dm, 1.0f, dX, q.dm));
-    SSM_TRY(gemm(true, false, q.di, q.dm, q.T, dxi, q.di, X, q.dm, 0.0f, g->dW_in, q.dm, true));
-    return gemm(true, false, q.di, q.dm, q.T, dz, q.di, X, q.dm, 0.0f, g->dW_in + (size_t)q.di * q.dm, q.dm,
-                true);
+    SSM_TRY(wgrad(gemm, q.di, q.dm, q.T, dxi, q.di, X, q.dm, g->dW_in, part, q.esz, stream, timing));
+    return wgrad(gemm, q.di, q.dm, q.T, dz, q.di, X, q.dm, g->dW_in + (size_t)q.di * q.dm, part, q.esz, stream,
+                 timing);
 }
 
 }  // extern "C"

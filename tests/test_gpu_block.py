@@ -122,3 +122,9 @@ def test_block_inference_forward_matches_training_forward(ctx):
     Y2, s2 = ssm.ssm_block_fwd(ctx, Xd, pd, training=False)
     torch.cuda.synchronize()
     assert s2 is None and torch.equal(Y1, Y2)
+
+
+def test_block_f32_split_weight_gradients(ctx):
+    # 16384 tokens: the weight gradients run as 4 token chunks summed in order
+    X, p, dY = W.make_block_inputs(4, 4096, 64, 128, 16, 8, 4, seed=57)
+    _check(ctx, X, p, dY, torch.float32, F32_TOL)
