@@ -356,7 +356,8 @@ def ssm_conv1d_step(ring, x, w, bias=None, *, y=None, stream=None, timing=None):
 
 
 # ---------------------------------------------------------------- Mamba block
-BLOCK_LIB_PATH = os.path.join(_HERE, "libssmblock.so")
+# SSM_BLOCK_LIB may point at another build of the block library (A/B timing).
+BLOCK_LIB_PATH = os.environ.get("SSM_BLOCK_LIB") or os.path.join(_HERE, "libssmblock.so")
 _block_lib = None
 BLOCK_PARAMS = ("W_in", "conv_w", "conv_b", "W_x", "W_dt", "dt_bias", "A_log", "D", "W_out")
 
@@ -457,7 +458,11 @@ def ssm_block_fwd(ctx, X, params, *, training=True, Y=None, stream=None, timing=
     saved = None
     if training:
         saved = torch.empty(lib.ssm_block_saved_bytes(ctypes.byref(dm)), dtype=torch.uint8, device=dev)
-    nws = lib.ssm_block_fwd_workspace_bytes(ctypes.byref(dm))
+        # a training forward needs only the scan's part of the workspace
+        nws = _lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(dims(dm.batch, dm.seqlen, dm.d_inner, dm.d_state,
+                                                                  X.dtype)))
+    else:
+        nws = lib.ssm_block_fwd_workspace_bytes(ctypes.byref(dm))
     ws = _workspace(nws, dev)
     rc = lib.ssm_block_fwd(ctx.ptr, ctypes.byref(dm), _ptr(X), ctypes.byref(pp), _ptr(Y), _ptr(saved), _ptr(ws),
                            nws, _stream(dev, stream), _timing_ptr(timing))

@@ -12,9 +12,8 @@
 //
 // Activations are token-major [T, features] (T = batch*seqlen), the layout the
 // conv and scan kernels read, so every projection is one row-major GEMM with
-// no transposes of data; x_proj's B and C columns are split into the dense
-// [T, 16] arrays the scan takes (and joined back for the backward) by a small
-// copy kernel.
+// no transposes of data; x_proj's output columns are split into dense dt_low,
+// B and C arrays (and joined back for the backward) by a small copy kernel.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 #include <stdint.h>
@@ -93,7 +92,7 @@ struct Carve {
 // Activations the backward needs (the forward's intermediates and the scan's
 // checkpoints).
 struct Saved {
-    size_t xi, z, xc, proj, Bm, Cm, dt, ys, ckpt, total;
+    size_t xi, z, xc, proj, dtl, Bm, Cm, dt, ys, ckpt, total;
 };
 Saved saved_layout(const Plan& p) {
     Carve c;
@@ -103,6 +102,7 @@ Saved saved_layout(const Plan& p) {
     s.z = c.take(act);
     s.xc = c.take(act);
     s.proj = c.take((size_t)p.T * p.P * p.esz);
+    s.dtl = c.take((size_t)p.T * p.R * p.esz);
     s.Bm = c.take((size_t)p.T * p.N * p.esz);
     s.Cm = c.take((size_t)p.T * p.N * p.esz);
     s.dt = c.take(act);
@@ -113,18 +113,19 @@ Saved saved_layout(const Plan& p) {
     return s;
 }
 
-// Forward workspace: the intermediates (used when no `saved` buffer is given)
-// and the scan's own workspace.
+// Forward workspace: the scan's own workspace, then room for the intermediates,
+// which is used only when no `saved` buffer is given (inference).
 struct FwdWs {
-    size_t act, scan, total;
+    size_t scan, act, training, total;
 };
 FwdWs fwd_ws(const Plan& p) {
     Carve c;
     FwdWs w;
-    const Saved s = saved_layout(p);
-    w.act = c.take(s.ckpt);  // everything before the checkpoints
     const ssm_dims sd = scan_dims(p);
     w.scan = c.take(ssm_scan_fwd_workspace_bytes(&sd));
+    w.training = c.off;
+    const Saved s = saved_layout(p);
+    w.act = c.take(s.ckpt);  // everything before the checkpoints
     w.total = c.off;
     return w;
 }
@@ -141,7 +142,7 @@ int64_t wgrad_splits(int64_t m, int64_t n, int64_t T) {
 }
 
 struct BwdWs {
-    size_t dys, dxc, ddt, dB, dC, dz, dproj, dxi, conv, scan, part, total;
+    size_t dys, dxc, ddt, ddtl, dB, dC, dz, dproj, dxi, conv, scan, part, total;
 };
 BwdWs bwd_ws(const Plan& p) {
     Carve c;
@@ -150,6 +151,7 @@ BwdWs bwd_ws(const Plan& p) {
     w.dys = c.take(act);
     w.dxc = c.take(act);
     w.ddt = c.take(act);
+    w.ddtl = c.take((size_t)p.T * p.R * p.esz);
     w.dB = c.take((size_t)p.T * p.N * p.esz);
     w.dC = c.take((size_t)p.T * p.N * p.esz);
     w.dz = c.take(act);
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(WG) void k_sum_parts(const float* __restrict__ part
 // Row-major f32 weight gradient C[m, n] = A^T B over T tokens, A [T, m] (lda),
 // B [T, n] (ldb), with the tokens split as described at wgrad_splits.
 ssm_status wgrad(const Gemm& g, int64_t m, int64_t n, int64_t T, const void* A, int64_t lda, const void* B,
-                 int64_t ldb, float* C, float* part, size_t esz, hipStream_t s, ssm_timing* tm) {
+                 int64_t ldb, float* C, float* part, hipStream_t s, ssm_timing* tm) {
     const int64_t S = wgrad_splits(m, n, T);
     if (S == 1) return g(true, false, m, n, T, A, lda, B, ldb, 0.0f, C, n, true);
     const int64_t Tc = T / S;
@@ -219,7 +221,6 @@ ssm_status wgrad(const Gemm& g, int64_t m, int64_t n, int64_t T, const void* A, 
         (rocblas_int)lda, (rocblas_stride)(Tc * lda), &beta, part, rocblas_datatype_f32_r, (rocblas_int)n,
         (rocblas_stride)(m * n), part, rocblas_datatype_f32_r, (rocblas_int)n, (rocblas_stride)(m * n),
         (rocblas_int)S, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-    (void)esz;
     if (st != rocblas_status_success) return SSM_E_LAUNCH;
     ssm::Launcher launch{s, tm};
     const int64_t mn = m * n;
@@ -227,45 +228,55 @@ ssm_status wgrad(const Gemm& g, int64_t m, int64_t n, int64_t T, const void* A, 
                   (const float*)part, C, mn, (int)S);
 }
 
-// ------------------------------------------------------------------ B/C columns
-// proj [T, R + 2N] -> B, C [T, N] (forward) and back (backward, into dproj).
+// ------------------------------------------------------------------ x_proj columns
+// proj [T, R + 2N] -> dt_low [T, R], B [T, N], C [T, N] (forward), and the
+// gradients back into dproj (backward).  Dense copies: the dt_proj GEMMs and the
+// scan then read unit-stride rows.
 template <typename T>
-__global__ __launch_bounds__(WG) void k_split_bc(const T* __restrict__ proj, T* __restrict__ Bm,
-                                                 T* __restrict__ Cm, int64_t n, int R, int N) {
+__global__ __launch_bounds__(WG) void k_split_proj(const T* __restrict__ proj, T* __restrict__ dtl,
+                                                   T* __restrict__ Bm, T* __restrict__ Cm, int64_t n, int R,
+                                                   int N) {
     const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
     if (i >= n) return;
-    const int64_t t = i / (2 * N);
-    const int j = (int)(i % (2 * N));
-    const T v = proj[t * (R + 2 * N) + R + j];
-    if (j < N) Bm[t * N + j] = v;
-    else Cm[t * N + (j - N)] = v;
+    const int P = R + 2 * N;
+    const int64_t t = i / P;
+    const int j = (int)(i % P);
+    const T v = proj[i];
+    if (j < R) dtl[t * R + j] = v;
+    else if (j < R + N) Bm[t * N + (j - R)] = v;
+    else Cm[t * N + (j - R - N)] = v;
 }
 
 template <typename T>
-__global__ __launch_bounds__(WG) void k_join_bc(const T* __restrict__ dB, const T* __restrict__ dC,
-                                                T* __restrict__ dproj, int64_t n, int R, int N) {
+__global__ __launch_bounds__(WG) void k_join_proj(const T* __restrict__ ddtl, const T* __restrict__ dB,
+                                                  const T* __restrict__ dC, T* __restrict__ dproj, int64_t n,
+                                                  int R, int N) {
     const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
     if (i >= n) return;
-    const int64_t t = i / (2 * N);
-    const int j = (int)(i % (2 * N));
-    dproj[t * (R + 2 * N) + R + j] = j < N ? dB[t * N + j] : dC[t * N + (j - N)];
+    const int P = R + 2 * N;
+    const int64_t t = i / P;
+    const int j = (int)(i % P);
+    dproj[i] = j < R ? ddtl[t * R + j] : (j < R + N ? dB[t * N + (j - R)] : dC[t * N + (j - R - N)]);
 }
 
-ssm_status launch_bc(const Plan& p, bool split, const void* a, const void* b, void* c, hipStream_t s,
-                     ssm_timing* tm) {
+template <typename T>
+ssm_status launch_proj_t(const Plan& p, bool split, const void* a, const void* b, const void* c, void* d,
+                         hipStream_t s, ssm_timing* tm) {
     ssm::Launcher launch{s, tm};
-    const int64_t n = p.T * 2 * p.N;
+    const int64_t n = p.T * p.P;
     const dim3 grid((unsigned)((n + WG - 1) / WG));
-    if (p.io == SSM_F32) {
-        return split ? launch(SSM_K_BLOCK_BC, k_split_bc<float>, grid, dim3(WG), (const float*)a, (float*)b,
-                              (float*)c, n, (int)p.R, (int)p.N)
-                     : launch(SSM_K_BLOCK_BC, k_join_bc<float>, grid, dim3(WG), (const float*)a, (const float*)b,
-                              (float*)c, n, (int)p.R, (int)p.N);
-    }
-    return split ? launch(SSM_K_BLOCK_BC, k_split_bc<bf16_t>, grid, dim3(WG), (const bf16_t*)a, (bf16_t*)b,
-                          (bf16_t*)c, n, (int)p.R, (int)p.N)
-                 : launch(SSM_K_BLOCK_BC, k_join_bc<bf16_t>, grid, dim3(WG), (const bf16_t*)a, (const bf16_t*)b,
-                          (bf16_t*)c, n, (int)p.R, (int)p.N);
+    if (split)  // a = proj -> b = dt_low, c = B, d = C
+        return launch(SSM_K_BLOCK_BC, k_split_proj<T>, grid, dim3(WG), (const T*)a, (T*)b, (T*)c, (T*)d, n,
+                      (int)p.R, (int)p.N);
+    // a = d dt_low, b = dB, c = dC -> d = dproj
+    return launch(SSM_K_BLOCK_BC, k_join_proj<T>, grid, dim3(WG), (const T*)a, (const T*)b, (const T*)c, (T*)d,
+                  n, (int)p.R, (int)p.N);
+}
+
+ssm_status launch_proj(const Plan& p, bool split, const void* a, const void* b, const void* c, void* d,
+                       hipStream_t s, ssm_timing* tm) {
+    return p.io == SSM_F32 ? launch_proj_t<float>(p, split, a, b, c, d, s, tm)
+                           : launch_proj_t<bf16_t>(p, split, a, b, c, d, s, tm);
 }
 
 bool any_misaligned(std::initializer_list<const void*> ptrs) {
@@ -326,13 +337,14 @@ ssm_status ssm_block_fwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
                         p->D, p->W_out}))
         return SSM_E_ALIGN;
     const FwdWs w = fwd_ws(q);
-    if (!ws || ws_bytes < w.total) return SSM_E_WORKSPACE;
+    const size_t need = saved ? w.training : w.total;
+    if (need > 0 && (!ws || ws_bytes < need)) return SSM_E_WORKSPACE;
     (void)hipGetLastError();
     if (rocblas_set_stream(ctx->h, stream) != rocblas_status_success) return SSM_E_LAUNCH;
     const Saved s = saved_layout(q);
     char* act = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + w.act;
-    void *xi = act + s.xi, *z = act + s.z, *xc = act + s.xc, *proj = act + s.proj, *Bm = act + s.Bm,
-         *Cm = act + s.Cm, *dt = act + s.dt, *ys = act + s.ys;
+    void *xi = act + s.xi, *z = act + s.z, *xc = act + s.xc, *proj = act + s.proj, *dtl = act + s.dtl,
+         *Bm = act + s.Bm, *Cm = act + s.Cm, *dt = act + s.dt, *ys = act + s.ys;
     float* ckpt = saved ? reinterpret_cast<float*>(act + s.ckpt) : nullptr;
     const rocblas_datatype io_t = q.io == SSM_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
     const Gemm gemm{ctx->h, io_t, io_t};
@@ -343,11 +355,11 @@ ssm_status ssm_block_fwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     const ssm_conv_dims cd = conv_dims(q);
     SSM_TRY(ssm_conv1d_fwd(&cd, xi, p->conv_w, p->conv_b, nullptr, xc, nullptr, stream, timing));
     SSM_TRY(gemm(false, true, q.T, q.P, q.di, xc, q.di, p->W_x, q.di, 0.0f, proj, q.P));
-    SSM_TRY(launch_bc(q, true, proj, Bm, Cm, stream, timing));
-    SSM_TRY(gemm(false, true, q.T, q.di, q.R, proj, q.P, p->W_dt, q.R, 0.0f, dt, q.di));
+    SSM_TRY(launch_proj(q, true, proj, dtl, Bm, Cm, stream, timing));
+    SSM_TRY(gemm(false, true, q.T, q.di, q.R, dtl, q.R, p->W_dt, q.R, 0.0f, dt, q.di));
     const ssm_dims sd = scan_dims(q);
     SSM_TRY(ssm_scan_fwd(&sd, xc, dt, Bm, Cm, z, p->A_log, p->D, p->dt_bias, nullptr, ys, nullptr, ckpt,
-                         static_cast<char*>(ws) + w.scan, w.total - w.scan, stream, timing));
+                         ws, w.training, stream, timing));
     return gemm(false, true, q.T, q.dm, q.di, ys, q.di, p->W_out, q.di, 0.0f, Y, q.dm);
 }
 
@@ -374,30 +386,30 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     if (rocblas_set_stream(ctx->h, stream) != rocblas_status_success) return SSM_E_LAUNCH;
     const Saved s = saved_layout(q);
     const char* act = static_cast<const char*>(saved);
-    const void *xi = act + s.xi, *z = act + s.z, *xc = act + s.xc, *proj = act + s.proj, *Bm = act + s.Bm,
+    const void *xi = act + s.xi, *z = act + s.z, *xc = act + s.xc, *dtl = act + s.dtl, *Bm = act + s.Bm,
                *Cm = act + s.Cm, *dt = act + s.dt, *ys = act + s.ys;
     const float* ckpt = reinterpret_cast<const float*>(act + s.ckpt);
     char* wb = static_cast<char*>(ws);
-    void *dys = wb + w.dys, *dxc = wb + w.dxc, *ddt = wb + w.ddt, *dB = wb + w.dB, *dC = wb + w.dC,
-         *dz = wb + w.dz, *dproj = wb + w.dproj, *dxi = wb + w.dxi;
+    void *dys = wb + w.dys, *dxc = wb + w.dxc, *ddt = wb + w.ddt, *ddtl = wb + w.ddtl, *dB = wb + w.dB,
+         *dC = wb + w.dC, *dz = wb + w.dz, *dproj = wb + w.dproj, *dxi = wb + w.dxi;
     const rocblas_datatype io_t = q.io == SSM_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
     const Gemm gemm{ctx->h, io_t, io_t};
     // out_proj
     SSM_TRY(gemm(false, false, q.T, q.di, q.dm, dY, q.dm, p->W_out, q.di, 0.0f, dys, q.di));
     float* part = reinterpret_cast<float*>(wb + w.part);
-    SSM_TRY(wgrad(gemm, q.dm, q.di, q.T, dY, q.dm, ys, q.di, g->dW_out, part, q.esz, stream, timing));
+    SSM_TRY(wgrad(gemm, q.dm, q.di, q.T, dY, q.dm, ys, q.di, g->dW_out, part, stream, timing));
     // scan
     const ssm_dims sd = scan_dims(q);
     SSM_TRY(ssm_scan_bwd(&sd, xc, dt, Bm, Cm, z, p->A_log, p->D, p->dt_bias, nullptr, ckpt, dys, dxc, ddt, dB,
                          dC, dz, g->dA_log, g->dD, g->ddt_bias, nullptr, wb + w.scan, w.total - w.scan, stream,
                          timing));
-    // dt_proj: d dt_low lands in the first R columns of dproj; x_proj's B/C columns follow
-    SSM_TRY(gemm(false, false, q.T, q.R, q.di, ddt, q.di, p->W_dt, q.R, 0.0f, dproj, q.P));
-    SSM_TRY(wgrad(gemm, q.di, q.R, q.T, ddt, q.di, proj, q.P, g->dW_dt, part, q.esz, stream, timing));
-    SSM_TRY(launch_bc(q, false, dB, dC, dproj, stream, timing));
+    // dt_proj, then x_proj's gradient rows [d dt_low | dB | dC]
+    SSM_TRY(gemm(false, false, q.T, q.R, q.di, ddt, q.di, p->W_dt, q.R, 0.0f, ddtl, q.R));
+    SSM_TRY(wgrad(gemm, q.di, q.R, q.T, ddt, q.di, dtl, q.R, g->dW_dt, part, stream, timing));
+    SSM_TRY(launch_proj(q, false, ddtl, dB, dC, dproj, stream, timing));
     // x_proj: dxc += dproj W_x
     SSM_TRY(gemm(false, false, q.T, q.di, q.P, dproj, q.P, p->W_x, q.di, 1.0f, dxc, q.di));
-    SSM_TRY(wgrad(gemm, q.P, q.di, q.T, dproj, q.P, xc, q.di, g->dW_x, part, q.esz, stream, timing));
+    SSM_TRY(wgrad(gemm, q.P, q.di, q.T, dproj, q.P, xc, q.di, g->dW_x, part, stream, timing));
     // conv1d + SiLU
     const ssm_conv_dims cd = conv_dims(q);
     SSM_TRY(ssm_conv1d_bwd(&cd, xi, p->conv_w, p->conv_b, nullptr, dxc, dxi, g->dconv_w, g->dconv_b, nullptr,
@@ -407,9 +419,8 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     const size_t half = (size_t)q.di * q.dm * q.esz;
     SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dxi, q.di, W_in, q.dm, 0.0f, dX, q.dm));
     SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dz, q.di, W_in + half, q.dm, 1.0f, dX, q.dm));
-    SSM_TRY(wgrad(gemm, q.di, q.dm, q.T, dxi, q.di, X, q.dm, g->dW_in, part, q.esz, stream, timing));
-    return wgrad(gemm, q.di, q.dm, q.T, dz, q.di, X, q.dm, g->dW_in + (size_t)q.di * q.dm, part, q.esz, stream,
-                 timing);
+    SSM_TRY(wgrad(gemm, q.di, q.dm, q.T, dxi, q.di, X, q.dm, g->dW_in, part, stream, timing));
+    return wgrad(gemm, q.di, q.dm, q.T, dz, q.di, X, q.dm, g->dW_in + (size_t)q.di * q.dm, part, stream, timing);
 }
 
 }  // extern "C"

@@ -246,9 +246,9 @@ def test_block_sizes():
     d = _bdims()
     T, di, P = 2 * 64, 64, 4 + 32
     act = T * di * 4
-    # xi, z, xc, dt, y_s [T, d_inner], proj [T, dt_rank + 32], B and C [T, 16], then
-    # the scan checkpoints (every piece a multiple of 256 bytes here)
-    assert blib.ssm_block_saved_bytes(ctypes.byref(d)) == 5 * act + T * P * 4 + 2 * T * 16 * 4 + \
+    # xi, z, xc, dt, y_s [T, d_inner], proj [T, dt_rank + 32], dt_low [T, dt_rank], B and
+    # C [T, 16], then the scan checkpoints (every piece a multiple of 256 bytes here)
+    assert blib.ssm_block_saved_bytes(ctypes.byref(d)) == 5 * act + T * P * 4 + T * 4 * 4 + 2 * T * 16 * 4 + \
         lib.ssm_scan_ckpt_bytes(ctypes.byref(_dims(2, 64, 64)))
     for bad in (_bdims(b=0), _bdims(L=0), _bdims(dm=12), _bdims(di=60), _bdims(n=8), _bdims(k=5),
                 _bdims(r=0), _bdims(io=4)):
