@@ -85,7 +85,10 @@ ssm_status ssm_block_create(ssm_block_ctx **ctx);
 void ssm_block_destroy(ssm_block_ctx *ctx);
 
 /* Bytes of the activations a training forward keeps for the backward, and of
- * the per-call workspaces; 0 for invalid dims. */
+ * the per-call workspaces; 0 for invalid dims.  The forward workspace size is
+ * what an inference call (saved == NULL) needs; a training call uses only its
+ * leading part, the scan's workspace (ssm_scan_fwd_workspace_bytes of
+ * {batch, seqlen, d_inner, d_state, io_dtype}), and accepts a buffer of that size. */
 size_t ssm_block_saved_bytes(const ssm_block_dims *dims);
 size_t ssm_block_fwd_workspace_bytes(const ssm_block_dims *dims);
 size_t ssm_block_bwd_workspace_bytes(const ssm_block_dims *dims);
