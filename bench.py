@@ -35,7 +35,9 @@ CSRC = os.path.join(ROOT, "selective_state_space_04_amd", "csrc")
 TRAFFIC = {"scan": (os.path.join(CSRC, "ssm_scan.hip"),
                     os.path.join(ROOT, "profiles", "c4_mamba2p8b_bf16_traffic.txt")),
            "conv1d": (os.path.join(CSRC, "ssm_conv1d.hip"),
-                      os.path.join(ROOT, "profiles", "conv_mamba2p8b_bf16_traffic.txt"))}
+                      os.path.join(ROOT, "profiles", "conv_mamba2p8b_bf16_traffic.txt")),
+           "decode": (os.path.join(CSRC, "ssm_scan.hip"),
+                      os.path.join(ROOT, "profiles", "c5_decode_step_traffic.txt"))}
 
 # Algorithmic f32 flops per element (b,t,d,n), FMA = 2, mul/add/exp = 1.
 #  forward main : exp(dt*A) (mul + exp), dt*x*B (mul), h update (FMA), C.h (FMA)  = 7
@@ -252,6 +254,8 @@ def decode_bench(args):
     A_log, Dp, bias = (torch.from_numpy(inp[k]).to(dev) for k in ("A_log", "D", "dt_bias"))
     h = torch.zeros(B, D, N, device=dev)
     ys = torch.empty(L, B, D, device=dev)
+    if args.copy_probe:
+        copy_probe(dev)
 
     def run():
         for t in range(L):
@@ -308,6 +312,7 @@ def decode_bench(args):
     elems = B * D * N * L
     per_step = B * D * N * 4 * 2 + 4 * B * D * 4 + 2 * B * N * 4 + 4 * D * (N + 2)
     gbps = per_step / (kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic("k_step", "decode")
     line = {
         "metric": "selective-scan decode elements(B\u00b7D\u00b7N per token)/s and achieved HBM GB/s",
         "value": elems / (eager_ms * 1e-3), "unit": "elements/s", "n_gpus": 1, "steps": L, "warmup": 1,
@@ -319,7 +324,7 @@ def decode_bench(args):
         "total_ms": {"eager": round(eager_ms, 3), "graph": round(graph_ms, 3)},
         "graph": {"value": elems / (graph_ms * 1e-3), "replays_bitwise_equal_eager": replays},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_step",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": "k_step",
                      "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes_per_launch": per_step},
         "cpu_baseline": None,
     }
