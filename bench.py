@@ -66,7 +66,7 @@ def parse():
                          "conv1d + SiLU fwd+bwd in front of it, on the same batch/seqlen/d_inner; "
                          "decode: 1024 single-token steps at batch 256 x d_inner 5120, eager and "
                          "replayed from a captured HIP graph; block: one Mamba block (projections on "
-                         "rocBLAS around the conv and the scan) fwd+bwd at the 2.8B layer shape")
+                         "hipBLASLt around the conv and the scan) fwd+bwd at the 2.8B layer shape")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to calibrate "
                          "profiler FETCH_SIZE / WRITE_SIZE counters")
@@ -423,7 +423,7 @@ def block_bench(args):
         "gemm": {"ms": round(gemm_ms, 4), "flops": gemm_flops,
                  "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                              "traffic": None, "kernel": "rocBLAS GEMMs (15 per step, aggregate)"}},
+                              "traffic": None, "kernel": "hipBLASLt GEMMs (15 per step, aggregate)"}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -13,7 +13,7 @@
  *     the batch;
  *   - the CUDA backward commit sends the four projections (forward and their
  *     gradient GEMMs) to a vendor BLAS and leaves the rest on the host; here the
- *     projections run on rocBLAS and the conv and the scan on this project's
+ *     projections run on hipBLASLt and the conv and the scan on this project's
  *     kernels (ssm_conv1d.h, ssm_scan.h), all on the caller's stream.
  * Readings: projections are bias-free, y = x W^T with [out, in] weights; in_proj's
  * first d_inner outputs feed the conv, the next d_inner are the gate z; x_proj's
@@ -23,8 +23,10 @@
  * Conventions (as in ssm_scan.h): DEVICE pointers, dense row-major, 16-byte
  * aligned, caller-owned; arguments are checked on the host before any launch;
  * work is ordered on `stream`.  Exceptions to "allocates nothing": the context
- * owns a rocBLAS handle (created by ssm_block_create), and rocBLAS manages that
- * handle's own device memory.  A context may be used by one thread at a time.
+ * owns a hipBLASLt handle (created by ssm_block_create), and hipBLASLt manages
+ * that handle's own device memory; the context also keeps, per GEMM shape seen,
+ * the descriptors and the algorithm the library's heuristic chose (host memory).
+ * A context may be used by one thread at a time.
  *   - Layouts (T = batch*seqlen tokens, dm = d_model, di = d_inner, N = d_state,
  *     R = dt_rank, K = d_conv, P = R + 2N):
  *       X, Y, dX, dY        : [batch, seqlen, dm]   io dtype
@@ -79,18 +81,20 @@ typedef struct { /* all f32, overwritten */
     float *dW_in, *dconv_w, *dconv_b, *dW_x, *dW_dt, *ddt_bias, *dA_log, *dD, *dW_out;
 } ssm_block_grads;
 
-/* Creates a context on the current HIP device (one rocBLAS handle).  Returns
+/* Creates a context on the current HIP device (one hipBLASLt handle).  Returns
  * SSM_E_LAUNCH if the handle cannot be created. */
 ssm_status ssm_block_create(ssm_block_ctx **ctx);
 void ssm_block_destroy(ssm_block_ctx *ctx);
 
 /* Bytes of the activations a training forward keeps for the backward, and of
- * the per-call workspaces; 0 for invalid dims.  The forward workspace size is
- * what an inference call (saved == NULL) needs; a training call uses only its
- * leading part, the scan's workspace (ssm_scan_fwd_workspace_bytes of
- * {batch, seqlen, d_inner, d_state, io_dtype}), and accepts a buffer of that size. */
+ * the per-call workspaces; 0 for invalid dims.  Every workspace starts with
+ * 64 MiB for the projections' GEMMs.  ssm_block_fwd_workspace_bytes is what an
+ * inference call (saved == NULL) needs; a training call uses only the leading
+ * ssm_block_fwd_training_workspace_bytes of it (the GEMMs' part and the scan's
+ * workspace) and accepts a buffer of that size. */
 size_t ssm_block_saved_bytes(const ssm_block_dims *dims);
 size_t ssm_block_fwd_workspace_bytes(const ssm_block_dims *dims);
+size_t ssm_block_fwd_training_workspace_bytes(const ssm_block_dims *dims);
 size_t ssm_block_bwd_workspace_bytes(const ssm_block_dims *dims);
 
 /* Forward: Y = block(X).  `saved` (ssm_block_saved_bytes, nullable for

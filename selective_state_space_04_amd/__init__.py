@@ -377,7 +377,7 @@ class BlockGrads(ctypes.Structure):
 
 
 def block_library():
-    """libssmblock.so (the Mamba block: projections on rocBLAS around this
+    """libssmblock.so (the Mamba block: projections on hipBLASLt around this
     library's conv and scan kernels), loaded on first use."""
     global _block_lib
     if _block_lib is not None:
@@ -391,7 +391,8 @@ def block_library():
     lib.ssm_block_create.restype = ctypes.c_int
     lib.ssm_block_destroy.argtypes = [P]
     lib.ssm_block_destroy.restype = None
-    for fn in ("ssm_block_saved_bytes", "ssm_block_fwd_workspace_bytes", "ssm_block_bwd_workspace_bytes"):
+    for fn in ("ssm_block_saved_bytes", "ssm_block_fwd_workspace_bytes", "ssm_block_fwd_training_workspace_bytes",
+               "ssm_block_bwd_workspace_bytes"):
         getattr(lib, fn).argtypes = [DP]
         getattr(lib, fn).restype = SZ
     lib.ssm_block_fwd.argtypes = [P, DP, P, ctypes.POINTER(BlockParams), P, P, P, SZ, P,
@@ -405,7 +406,7 @@ def block_library():
 
 
 class BlockContext:
-    """A rocBLAS handle on the current device for ssm_block_fwd / ssm_block_bwd."""
+    """A hipBLASLt handle on the current device for ssm_block_fwd / ssm_block_bwd."""
 
     def __init__(self):
         self._lib = block_library()
@@ -458,9 +459,7 @@ def ssm_block_fwd(ctx, X, params, *, training=True, Y=None, stream=None, timing=
     saved = None
     if training:
         saved = torch.empty(lib.ssm_block_saved_bytes(ctypes.byref(dm)), dtype=torch.uint8, device=dev)
-        # a training forward needs only the scan's part of the workspace
-        nws = _lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(dims(dm.batch, dm.seqlen, dm.d_inner, dm.d_state,
-                                                                  X.dtype)))
+        nws = lib.ssm_block_fwd_training_workspace_bytes(ctypes.byref(dm))
     else:
         nws = lib.ssm_block_fwd_workspace_bytes(ctypes.byref(dm))
     ws = _workspace(nws, dev)

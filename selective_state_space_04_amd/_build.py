@@ -1,6 +1,6 @@
 """Compiles libssmscan.so (HIP, gfx950 only: the selective scan and the conv1d
 in front of it) and libssmblock.so (one Mamba block: those kernels plus the
-projections on rocBLAS) in-tree with hipcc."""
+projections on hipBLASLt) in-tree with hipcc."""
 import os
 import subprocess
 
@@ -40,9 +40,9 @@ def _hipcc(cmd, out, verbose):
 
 def build(verbose=False, extra=()):
     """libssmscan.so (scan + conv1d kernels), then libssmblock.so (the Mamba block
-    on top of it and rocBLAS)."""
+    on top of it and hipBLASLt)."""
     _hipcc([HIPCC, *FLAGS, *extra, "-I", INCLUDE, *SRCS], LIB_PATH, verbose)
     _hipcc([HIPCC, *FLAGS, *extra, "-I", INCLUDE, BLOCK_SRC, "-L", HERE, "-lssmscan",
-            f"-L{ROCM_LIB}", "-lrocblas", "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{ROCM_LIB}"],
+            f"-L{ROCM_LIB}", "-lhipblaslt", "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{ROCM_LIB}"],
            BLOCK_LIB_PATH, verbose)
     return LIB_PATH

@@ -1,5 +1,5 @@
 // ssm_block.hip -- one Mamba block around the selective scan, on one MI355X:
-// the four projections on rocBLAS (bf16 or f32 operands, f32 accumulation), the
+// the four projections on hipBLASLt (bf16 or f32 operands, f32 accumulation), the
 // conv1d + SiLU and the scan on this project's kernels, everything on the
 // caller's stream.  Built as libssmblock.so on top of libssmscan.so.
 //
@@ -15,19 +15,31 @@
 // no transposes of data; x_proj's output columns are split into dense dt_low,
 // B and C arrays (and joined back for the backward) by a small copy kernel.
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
+#include <hipblaslt/hipblaslt.h>
 #include <stdint.h>
 
 #include <algorithm>
 #include <initializer_list>
+#include <vector>
 
 #include "ssm_block.h"
 #include "ssm_common.h"
 #include "ssm_conv1d.h"
 #include "ssm_scan.h"
 
+// One GEMM configuration: its descriptors and the algorithm hipBLASLt's
+// heuristic picked for it, kept for the life of the context.
+struct LtPlan {
+    int64_t key[11];
+    hipblasLtMatmulDesc_t op;
+    hipblasLtMatrixLayout_t a, b, c;
+    hipblasLtMatmulAlgo_t algo;
+    size_t ws;  // workspace bytes the algorithm uses
+};
+
 struct ssm_block_ctx {
-    rocblas_handle h;
+    hipblasLtHandle_t lt;
+    std::vector<LtPlan> plans;
 };
 
 namespace {
@@ -37,6 +49,7 @@ using ssm::misaligned;
 
 constexpr int WG = 256;
 constexpr int NS = 16;
+constexpr size_t GEMM_WS = (size_t)64 << 20;  // workspace offered to each GEMM
 
 struct Plan {
     int64_t Bt, L, T, dm, di, N, R, K, P;
@@ -113,14 +126,16 @@ Saved saved_layout(const Plan& p) {
     return s;
 }
 
-// Forward workspace: the scan's own workspace, then room for the intermediates,
-// which is used only when no `saved` buffer is given (inference).
+// Forward workspace: the GEMMs' workspace, the scan's own workspace, then room
+// for the intermediates, which is used only when no `saved` buffer is given
+// (inference).
 struct FwdWs {
-    size_t scan, act, training, total;
+    size_t gemm, scan, act, training, total;
 };
 FwdWs fwd_ws(const Plan& p) {
     Carve c;
     FwdWs w;
+    w.gemm = c.take(GEMM_WS);
     const ssm_dims sd = scan_dims(p);
     w.scan = c.take(ssm_scan_fwd_workspace_bytes(&sd));
     w.training = c.off;
@@ -142,11 +157,12 @@ int64_t wgrad_splits(int64_t m, int64_t n, int64_t T) {
 }
 
 struct BwdWs {
-    size_t dys, dxc, ddt, ddtl, dB, dC, dz, dproj, dxi, conv, scan, part, total;
+    size_t gemm, dys, dxc, ddt, ddtl, dB, dC, dz, dproj, dxi, conv, scan, part, total;
 };
 BwdWs bwd_ws(const Plan& p) {
     Carve c;
     BwdWs w;
+    w.gemm = c.take(GEMM_WS);
     const size_t act = (size_t)p.T * p.di * p.esz;
     w.dys = c.take(act);
     w.dxc = c.take(act);
@@ -176,23 +192,90 @@ BwdWs bwd_ws(const Plan& p) {
 // ------------------------------------------------------------------ GEMMs
 // Row-major C[m, n] (ldc) = opA(A) opB(B) + beta C, where opA(A) = A [m, k] (lda)
 // or, with ta, A^T for A stored [k, m]; opB(B) = B [k, n] (ldb) or, with tb, B^T
-// for B stored [n, k].  rocBLAS is column-major, so this is the column-major
-// product C^T = opB(B)^T opA(A)^T with the operands swapped.
+// for B stored [n, k].  hipBLASLt is column-major, so this is the column-major
+// product C^T = opB(B)^T opA(A)^T with the operands swapped.  `batch` > 1 runs
+// that many such products at element strides sA, sB, sC.  Each call may use up
+// to GEMM_WS bytes of the caller's workspace.
+bool set_batch(hipblasLtMatrixLayout_t l, int32_t batch, int64_t stride) {
+    if (batch <= 1) return true;
+    return hipblasLtMatrixLayoutSetAttribute(l, HIPBLASLT_MATRIX_LAYOUT_BATCH_COUNT, &batch, sizeof(batch)) ==
+               HIPBLAS_STATUS_SUCCESS &&
+           hipblasLtMatrixLayoutSetAttribute(l, HIPBLASLT_MATRIX_LAYOUT_STRIDED_BATCH_OFFSET, &stride,
+                                             sizeof(stride)) == HIPBLAS_STATUS_SUCCESS;
+}
+
+void destroy_plan(LtPlan& e) {
+    if (e.a) hipblasLtMatrixLayoutDestroy(e.a);
+    if (e.b) hipblasLtMatrixLayoutDestroy(e.b);
+    if (e.c) hipblasLtMatrixLayoutDestroy(e.c);
+    if (e.op) hipblasLtMatmulDescDestroy(e.op);
+}
+
+// The plan for one configuration, created (descriptors + heuristic query) on
+// first use.  Returns nullptr if hipBLASLt offers no algorithm for it.
+const LtPlan* get_plan(ssm_block_ctx* ctx, bool ta, bool tb, int64_t m, int64_t n, int64_t k, int64_t lda,
+                       int64_t ldb, int64_t ldc, hipDataType ab, hipDataType ct, int32_t batch, int64_t sA,
+                       int64_t sB, int64_t sC) {
+    const int64_t key[11] = {(int64_t)ta | ((int64_t)tb << 1) | ((int64_t)ab << 8) | ((int64_t)ct << 24),
+                             m, n, k, lda, ldb, ldc, batch, sA, sB, sC};
+    for (const LtPlan& e : ctx->plans)
+        if (std::equal(key, key + 11, e.key)) return &e;
+    LtPlan e{};
+    std::copy(key, key + 11, e.key);
+    bool ok = hipblasLtMatmulDescCreate(&e.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
+    const int32_t opa = tb ? HIPBLAS_OP_T : HIPBLAS_OP_N, opb = ta ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+    ok = ok &&
+         hipblasLtMatmulDescSetAttribute(e.op, HIPBLASLT_MATMUL_DESC_TRANSA, &opa, sizeof(opa)) ==
+             HIPBLAS_STATUS_SUCCESS &&
+         hipblasLtMatmulDescSetAttribute(e.op, HIPBLASLT_MATMUL_DESC_TRANSB, &opb, sizeof(opb)) ==
+             HIPBLAS_STATUS_SUCCESS;
+    // column-major: a = B viewed [n, k] (stored [k, n] or, with tb, [n, k] = a^T),
+    // b = A viewed [k, m], c = C viewed [n, m]
+    ok = ok && hipblasLtMatrixLayoutCreate(&e.a, ab, tb ? k : n, tb ? n : k, ldb) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&e.b, ab, ta ? m : k, ta ? k : m, lda) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&e.c, ct, n, m, ldc) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && set_batch(e.a, batch, sB) && set_batch(e.b, batch, sA) && set_batch(e.c, batch, sC);
+    // the heuristic's first choice within the workspace offered
+    hipblasLtMatmulPreference_t pref = nullptr;
+    ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
+    const uint64_t max_ws = GEMM_WS;
+    ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &max_ws,
+                                                     sizeof(max_ws)) == HIPBLAS_STATUS_SUCCESS;
+    constexpr int NREQ = 8;
+    hipblasLtMatmulHeuristicResult_t res[NREQ];
+    int got = 0;
+    ok = ok && hipblasLtMatmulAlgoGetHeuristic(ctx->lt, e.op, e.a, e.b, e.c, e.c, pref, NREQ, res, &got) ==
+                   HIPBLAS_STATUS_SUCCESS;
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    int pick = -1;
+    for (int r = 0; ok && r < got && pick < 0; ++r)
+        if (res[r].state == HIPBLAS_STATUS_SUCCESS && res[r].workspaceSize <= GEMM_WS) pick = r;
+    if (pick < 0) {
+        destroy_plan(e);
+        return nullptr;
+    }
+    e.algo = res[pick].algo;
+    e.ws = res[pick].workspaceSize;
+    ctx->plans.push_back(e);
+    return &ctx->plans.back();
+}
+
 struct Gemm {
-    rocblas_handle h;
-    rocblas_datatype ab, io_c;
+    ssm_block_ctx* ctx;
+    hipDataType ab, io_c;
+    hipStream_t s;
+    void* ws;  // GEMM_WS bytes
     ssm_status operator()(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
                           const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
-                          bool f32_out = false) const {
+                          bool f32_out = false, int32_t batch = 1, int64_t sA = 0, int64_t sB = 0,
+                          int64_t sC = 0) const {
         const float alpha = 1.0f;
-        const rocblas_datatype ct = f32_out ? rocblas_datatype_f32_r : io_c;
-        const rocblas_status st = rocblas_gemm_ex(
-            h, tb ? rocblas_operation_transpose : rocblas_operation_none,
-            ta ? rocblas_operation_transpose : rocblas_operation_none, (rocblas_int)n, (rocblas_int)m,
-            (rocblas_int)k, &alpha, B, ab, (rocblas_int)ldb, A, ab, (rocblas_int)lda, &beta, C, ct,
-            (rocblas_int)ldc, C, ct, (rocblas_int)ldc, rocblas_datatype_f32_r, rocblas_gemm_algo_standard,
-            0, 0);
-        return st == rocblas_status_success ? SSM_OK : SSM_E_LAUNCH;
+        const LtPlan* e = get_plan(ctx, ta, tb, m, n, k, lda, ldb, ldc, ab, f32_out ? HIP_R_32F : io_c, batch,
+                                   sA, sB, sC);
+        if (!e) return SSM_E_UNSUPPORTED;
+        const hipblasStatus_t st = hipblasLtMatmul(ctx->lt, e->op, &alpha, B, e->a, A, e->b, &beta, C, e->c, C,
+                                                   e->c, &e->algo, e->ws ? ws : nullptr, e->ws, s);
+        return st == HIPBLAS_STATUS_SUCCESS ? SSM_OK : SSM_E_LAUNCH;
     }
 };
 
@@ -209,20 +292,12 @@ __global__ __launch_bounds__(WG) void k_sum_parts(const float* __restrict__ part
 // Row-major f32 weight gradient C[m, n] = A^T B over T tokens, A [T, m] (lda),
 // B [T, n] (ldb), with the tokens split as described at wgrad_splits.
 ssm_status wgrad(const Gemm& g, int64_t m, int64_t n, int64_t T, const void* A, int64_t lda, const void* B,
-                 int64_t ldb, float* C, float* part, hipStream_t s, ssm_timing* tm) {
+                 int64_t ldb, float* C, float* part, ssm_timing* tm) {
     const int64_t S = wgrad_splits(m, n, T);
     if (S == 1) return g(true, false, m, n, T, A, lda, B, ldb, 0.0f, C, n, true);
     const int64_t Tc = T / S;
-    const float alpha = 1.0f, beta = 0.0f;
-    // column-major view as in Gemm: C^T [n, m] = B^T [n, Tc] . A [Tc, m] per chunk
-    const rocblas_status st = rocblas_gemm_strided_batched_ex(
-        g.h, rocblas_operation_none, rocblas_operation_transpose, (rocblas_int)n, (rocblas_int)m,
-        (rocblas_int)Tc, &alpha, B, g.ab, (rocblas_int)ldb, (rocblas_stride)(Tc * ldb), A, g.ab,
-        (rocblas_int)lda, (rocblas_stride)(Tc * lda), &beta, part, rocblas_datatype_f32_r, (rocblas_int)n,
-        (rocblas_stride)(m * n), part, rocblas_datatype_f32_r, (rocblas_int)n, (rocblas_stride)(m * n),
-        (rocblas_int)S, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-    if (st != rocblas_status_success) return SSM_E_LAUNCH;
-    ssm::Launcher launch{s, tm};
+    SSM_TRY(g(true, false, m, n, Tc, A, lda, B, ldb, 0.0f, part, n, true, (int32_t)S, Tc * lda, Tc * ldb, m * n));
+    ssm::Launcher launch{g.s, tm};
     const int64_t mn = m * n;
     return launch(SSM_K_BLOCK_BC, k_sum_parts, dim3((unsigned)((mn + WG - 1) / WG)), dim3(WG),
                   (const float*)part, C, mn, (int)S);
@@ -292,20 +367,16 @@ extern "C" {
 ssm_status ssm_block_create(ssm_block_ctx** ctx) {
     if (!ctx) return SSM_E_NULLPTR;
     *ctx = nullptr;
-    rocblas_handle h;
-    if (rocblas_create_handle(&h) != rocblas_status_success) return SSM_E_LAUNCH;
-    // no atomics inside GEMMs: repeated calls give bitwise identical results
-    if (rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed) != rocblas_status_success) {
-        rocblas_destroy_handle(h);
-        return SSM_E_LAUNCH;
-    }
-    *ctx = new ssm_block_ctx{h};
+    hipblasLtHandle_t lt;
+    if (hipblasLtCreate(&lt) != HIPBLAS_STATUS_SUCCESS) return SSM_E_LAUNCH;
+    *ctx = new ssm_block_ctx{lt, {}};
     return SSM_OK;
 }
 
 void ssm_block_destroy(ssm_block_ctx* ctx) {
     if (!ctx) return;
-    rocblas_destroy_handle(ctx->h);
+    for (LtPlan& e : ctx->plans) destroy_plan(e);
+    hipblasLtDestroy(ctx->lt);
     delete ctx;
 }
 
@@ -317,6 +388,11 @@ size_t ssm_block_saved_bytes(const ssm_block_dims* dims) {
 size_t ssm_block_fwd_workspace_bytes(const ssm_block_dims* dims) {
     if (check_block(dims) != SSM_OK) return 0;
     return fwd_ws(make_plan(dims)).total;
+}
+
+size_t ssm_block_fwd_training_workspace_bytes(const ssm_block_dims* dims) {
+    if (check_block(dims) != SSM_OK) return 0;
+    return fwd_ws(make_plan(dims)).training;
 }
 
 size_t ssm_block_bwd_workspace_bytes(const ssm_block_dims* dims) {
@@ -338,16 +414,15 @@ ssm_status ssm_block_fwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
         return SSM_E_ALIGN;
     const FwdWs w = fwd_ws(q);
     const size_t need = saved ? w.training : w.total;
-    if (need > 0 && (!ws || ws_bytes < need)) return SSM_E_WORKSPACE;
+    if (!ws || ws_bytes < need) return SSM_E_WORKSPACE;
     (void)hipGetLastError();
-    if (rocblas_set_stream(ctx->h, stream) != rocblas_status_success) return SSM_E_LAUNCH;
     const Saved s = saved_layout(q);
     char* act = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + w.act;
     void *xi = act + s.xi, *z = act + s.z, *xc = act + s.xc, *proj = act + s.proj, *dtl = act + s.dtl,
          *Bm = act + s.Bm, *Cm = act + s.Cm, *dt = act + s.dt, *ys = act + s.ys;
     float* ckpt = saved ? reinterpret_cast<float*>(act + s.ckpt) : nullptr;
-    const rocblas_datatype io_t = q.io == SSM_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const Gemm gemm{ctx->h, io_t, io_t};
+    const hipDataType io_t = q.io == SSM_BF16 ? HIP_R_16BF : HIP_R_32F;
+    const Gemm gemm{ctx, io_t, io_t, stream, static_cast<char*>(ws) + w.gemm};
     const char* W_in = static_cast<const char*>(p->W_in);
     const size_t half = (size_t)q.di * q.dm * q.esz;
     SSM_TRY(gemm(false, true, q.T, q.di, q.dm, X, q.dm, W_in, q.dm, 0.0f, xi, q.di));
@@ -359,7 +434,7 @@ ssm_status ssm_block_fwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     SSM_TRY(gemm(false, true, q.T, q.di, q.R, dtl, q.R, p->W_dt, q.R, 0.0f, dt, q.di));
     const ssm_dims sd = scan_dims(q);
     SSM_TRY(ssm_scan_fwd(&sd, xc, dt, Bm, Cm, z, p->A_log, p->D, p->dt_bias, nullptr, ys, nullptr, ckpt,
-                         ws, w.training, stream, timing));
+                         static_cast<char*>(ws) + w.scan, w.training - w.scan, stream, timing));
     return gemm(false, true, q.T, q.dm, q.di, ys, q.di, p->W_out, q.di, 0.0f, Y, q.dm);
 }
 
@@ -383,7 +458,6 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     const BwdWs w = bwd_ws(q);
     if (!ws || ws_bytes < w.total) return SSM_E_WORKSPACE;
     (void)hipGetLastError();
-    if (rocblas_set_stream(ctx->h, stream) != rocblas_status_success) return SSM_E_LAUNCH;
     const Saved s = saved_layout(q);
     const char* act = static_cast<const char*>(saved);
     const void *xi = act + s.xi, *z = act + s.z, *xc = act + s.xc, *dtl = act + s.dtl, *Bm = act + s.Bm,
@@ -392,12 +466,12 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     char* wb = static_cast<char*>(ws);
     void *dys = wb + w.dys, *dxc = wb + w.dxc, *ddt = wb + w.ddt, *ddtl = wb + w.ddtl, *dB = wb + w.dB,
          *dC = wb + w.dC, *dz = wb + w.dz, *dproj = wb + w.dproj, *dxi = wb + w.dxi;
-    const rocblas_datatype io_t = q.io == SSM_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const Gemm gemm{ctx->h, io_t, io_t};
+    const hipDataType io_t = q.io == SSM_BF16 ? HIP_R_16BF : HIP_R_32F;
+    const Gemm gemm{ctx, io_t, io_t, stream, wb + w.gemm};
     // out_proj
     SSM_TRY(gemm(false, false, q.T, q.di, q.dm, dY, q.dm, p->W_out, q.di, 0.0f, dys, q.di));
     float* part = reinterpret_cast<float*>(wb + w.part);
-    SSM_TRY(wgrad(gemm, q.dm, q.di, q.T, dY, q.dm, ys, q.di, g->dW_out, part, stream, timing));
+    SSM_TRY(wgrad(gemm, q.dm, q.di, q.T, dY, q.dm, ys, q.di, g->dW_out, part, timing));
     // scan
     const ssm_dims sd = scan_dims(q);
     SSM_TRY(ssm_scan_bwd(&sd, xc, dt, Bm, Cm, z, p->A_log, p->D, p->dt_bias, nullptr, ckpt, dys, dxc, ddt, dB,
@@ -405,11 +479,11 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
                          timing));
     // dt_proj, then x_proj's gradient rows [d dt_low | dB | dC]
     SSM_TRY(gemm(false, false, q.T, q.R, q.di, ddt, q.di, p->W_dt, q.R, 0.0f, ddtl, q.R));
-    SSM_TRY(wgrad(gemm, q.di, q.R, q.T, ddt, q.di, dtl, q.R, g->dW_dt, part, stream, timing));
+    SSM_TRY(wgrad(gemm, q.di, q.R, q.T, ddt, q.di, dtl, q.R, g->dW_dt, part, timing));
     SSM_TRY(launch_proj(q, false, ddtl, dB, dC, dproj, stream, timing));
     // x_proj: dxc += dproj W_x
     SSM_TRY(gemm(false, false, q.T, q.di, q.P, dproj, q.P, p->W_x, q.di, 1.0f, dxc, q.di));
-    SSM_TRY(wgrad(gemm, q.P, q.di, q.T, dproj, q.P, xc, q.di, g->dW_x, part, stream, timing));
+    SSM_TRY(wgrad(gemm, q.P, q.di, q.T, dproj, q.P, xc, q.di, g->dW_x, part, timing));
     // conv1d + SiLU
     const ssm_conv_dims cd = conv_dims(q);
     SSM_TRY(ssm_conv1d_bwd(&cd, xi, p->conv_w, p->conv_b, nullptr, dxc, dxi, g->dconv_w, g->dconv_b, nullptr,
@@ -419,8 +493,8 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     const size_t half = (size_t)q.di * q.dm * q.esz;
     SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dxi, q.di, W_in, q.dm, 0.0f, dX, q.dm));
     SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dz, q.di, W_in + half, q.dm, 1.0f, dX, q.dm));
-    SSM_TRY(wgrad(gemm, q.di, q.dm, q.T, dxi, q.di, X, q.dm, g->dW_in, part, stream, timing));
-    return wgrad(gemm, q.di, q.dm, q.T, dz, q.di, X, q.dm, g->dW_in + (size_t)q.di * q.dm, part, stream, timing);
+    SSM_TRY(wgrad(gemm, q.di, q.dm, q.T, dxi, q.di, X, q.dm, g->dW_in, part, timing));
+    return wgrad(gemm, q.di, q.dm, q.T, dz, q.di, X, q.dm, g->dW_in + (size_t)q.di * q.dm, part, timing);
 }
 
 }  // extern "C"

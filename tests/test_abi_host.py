@@ -40,7 +40,8 @@ def test_block_header_exports_present():
     blib = ssm.block_library()
     names = _declared_functions([BLOCK_HEADER])
     assert {"ssm_block_create", "ssm_block_destroy", "ssm_block_fwd", "ssm_block_bwd", "ssm_block_saved_bytes",
-            "ssm_block_fwd_workspace_bytes", "ssm_block_bwd_workspace_bytes"} <= set(names)
+            "ssm_block_fwd_workspace_bytes", "ssm_block_fwd_training_workspace_bytes",
+            "ssm_block_bwd_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(blib, n), f"{n} declared in ssm_block.h but not exported by libssmblock.so"
 
@@ -254,7 +255,15 @@ def test_block_sizes():
                 _bdims(r=0), _bdims(io=4)):
         assert blib.ssm_block_saved_bytes(ctypes.byref(bad)) == 0
         assert blib.ssm_block_fwd_workspace_bytes(ctypes.byref(bad)) == 0
+        assert blib.ssm_block_fwd_training_workspace_bytes(ctypes.byref(bad)) == 0
         assert blib.ssm_block_bwd_workspace_bytes(ctypes.byref(bad)) == 0
+    # every workspace leads with 64 MiB for the GEMMs; a training forward needs that
+    # and the scan's workspace, an inference forward also room for the intermediates
+    gemm = 64 << 20
+    scan = lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(_dims(2, 64, 64)))
+    assert blib.ssm_block_fwd_training_workspace_bytes(ctypes.byref(d)) == gemm + scan
+    assert blib.ssm_block_fwd_workspace_bytes(ctypes.byref(d)) > gemm + scan
+    assert blib.ssm_block_bwd_workspace_bytes(ctypes.byref(d)) > gemm
 
 
 def test_block_rejects_bad_arguments():
