@@ -61,12 +61,14 @@ def parse():
     ap.add_argument("--cpu-sample-channels", type=int, default=0,
                     help="channels the oracle baseline runs on (0 = all)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
-    ap.add_argument("--op", choices=("scan", "conv1d", "decode", "block"), default="scan",
+    ap.add_argument("--op", choices=("scan", "conv1d", "decode", "block", "train"), default="scan",
                     help="scan: the selective scan fwd+bwd (default); conv1d: the causal depthwise "
                          "conv1d + SiLU fwd+bwd in front of it, on the same batch/seqlen/d_inner; "
                          "decode: 1024 single-token steps at batch 256 x d_inner 5120, eager and "
                          "replayed from a captured HIP graph; block: one Mamba block (projections on "
                          "hipBLASLt around the conv and the scan) fwd+bwd at the 2.8B layer shape")
+    ap.add_argument("--dim", type=int, default=16,
+                    help="--op train: d_model of the one-block model (d_inner = 2 d_model)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (known bytes) to calibrate "
                          "profiler FETCH_SIZE / WRITE_SIZE counters")
@@ -445,6 +447,88 @@ def block_bench(args):
             f.write(out + "\n")
 
 
+def train_bench(args):
+    """Training steps/s of a one-block model (d_model = --dim, d_inner = 2 dim,
+    d_state 16, dt_rank ceil(dim/16), d_conv 4, f32): each step gathers a batch of
+    16 sequences x 128 tokens from a synthetic four-regime corpus, runs the block
+    forward, the next-step MSE loss and its gradient, the block backward and one
+    Adam update of all nine parameter tensors.  The block's forward and backward
+    are this library's calls; the loss and Adam are plain PyTorch ops."""
+    import numpy as np
+    import torch
+
+    import selective_state_space_04_amd as ssm
+    import workloads as W
+
+    dim, bsz, L, nseq = args.dim, 16, 128, 256
+    di, R = 2 * dim, -(-dim // 16)
+    dev = torch.device("cuda:0")
+    Xc, Yc = W.make_regime_corpus(nseq, L, dim, seed=0)
+    _, p0, _ = W.make_block_inputs(1, 1, dim, di, 16, R, 4, seed=1)
+    params = {k: torch.from_numpy(v).to(dev).clone() for k, v in p0.items()}
+    opt = torch.optim.Adam(list(params.values()), lr=2e-3, foreach=True)
+    Xd, Yd = torch.from_numpy(Xc).to(dev), torch.from_numpy(Yc).to(dev)
+    nsteps = args.warmup + args.steps
+    order = torch.from_numpy(np.random.default_rng(2).integers(0, nseq, (nsteps, bsz))).to(dev)
+    ctx = ssm.BlockContext()
+    losses = []
+
+    def step(i):
+        xb, yb = Xd[order[i]], Yd[order[i]]
+        Y, saved = ssm.ssm_block_fwd(ctx, xb, params)
+        diff = Y - yb
+        losses.append((diff * diff).mean())
+        g = ssm.ssm_block_bwd(ctx, xb, params, saved, diff * (2.0 / diff.numel()))
+        for k, t in params.items():
+            t.grad = g["d" + k]
+        opt.step()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.warmup, nsteps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    mse = [float(v) for v in losses]
+    line = {
+        "metric": "one-block training steps/s", "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"one Mamba block, d_model={dim} d_inner={di} d_state=16 dt_rank={R} d_conv=4, "
+                               f"batch {bsz} x {L} tokens of a synthetic four-regime corpus, next-step MSE, "
+                               f"Adam lr 2e-3, f32",
+                   "d_model": dim, "batch": bsz, "seqlen": L},
+        "mse_first": round(mse[0], 6), "mse_last": round(mse[-1], 6),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle.block import block_bwd
+        idx = order[0].cpu().numpy()
+        xb = np.ascontiguousarray(Xc[idx])
+        dY = np.ones_like(xb) * np.float32(2.0 / xb.size)
+        reps, t0 = 0, time.perf_counter()
+        while reps < 50 and time.perf_counter() - t0 < 5.0:
+            block_bwd(xb, p0, dY)  # forward and backward of one step's batch in f64
+            reps += 1
+        sec = (time.perf_counter() - t0) / reps
+        line["cpu_baseline"] = {"value": 1.0 / sec, "unit": "steps/s", "cores": oracle.num_threads(),
+                                "kind": "oracle",
+                                "sample": f"{reps} block forward+backward passes of one step's batch in f64, "
+                                          f"no optimizer ({sec * 1e3:.1f} ms each)"}
+    ctx.close()
+    out = json.dumps(line)
+    print(out, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(out + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -459,6 +543,9 @@ def main():
         return
     if args.op == "block":
         block_bench(args)
+        return
+    if args.op == "train":
+        train_bench(args)
         return
 
     import numpy as np

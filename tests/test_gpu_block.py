@@ -135,3 +135,28 @@ def test_block_f32_split_weight_gradients(ctx):
     # 16384 tokens: the weight gradients run as 4 token chunks summed in order
     X, p, dY = W.make_block_inputs(4, 4096, 64, 128, 16, 8, 4, seed=57)
     _check(ctx, X, p, dY, torch.float32, F32_TOL)
+
+
+def test_training_steps_reduce_the_loss(ctx):
+    """Adam on the block's own gradients lowers the next-step MSE on the synthetic
+    four-regime corpus (the training loop of bench.py --op train, 60 steps)."""
+    dim, di = 16, 32
+    X, Yt = W.make_regime_corpus(64, 64, dim, seed=3)
+    _, p0, _ = W.make_block_inputs(1, 1, dim, di, 16, 1, 4, seed=1)
+    dev = torch.device("cuda:0")
+    params = {k: torch.from_numpy(v).to(dev).clone() for k, v in p0.items()}
+    opt = torch.optim.Adam(list(params.values()), lr=2e-3)
+    Xd, Yd = torch.from_numpy(X).to(dev), torch.from_numpy(Yt).to(dev)
+    losses = []
+    for i in range(60):
+        sl = slice((i % 4) * 16, (i % 4) * 16 + 16)
+        xb, yb = Xd[sl].contiguous(), Yd[sl].contiguous()
+        Y, saved = ssm.ssm_block_fwd(ctx, xb, params)
+        diff = Y - yb
+        losses.append(float((diff * diff).mean()))
+        g = ssm.ssm_block_bwd(ctx, xb, params, saved, diff * (2.0 / diff.numel()))
+        for k, t in params.items():
+            t.grad = g["d" + k]
+        opt.step()
+    assert all(np.isfinite(losses))
+    assert np.mean(losses[-4:]) < 0.5 * np.mean(losses[:4]), losses

@@ -186,3 +186,39 @@ def make_block_config(name, *, seed=0):
     c = BLOCK_CONFIGS[name]
     return make_block_inputs(c["batch"], c["seqlen"], c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"],
                              c["d_conv"], seed=seed, bf16=c["io"] == "bf16")
+
+
+def make_regime_corpus(n_seq, seqlen, d_model, *, seed=0):
+    """Synthetic stand-in for a four-regime sequence corpus (the pages train on
+    one but do not publish it).  Sequence i follows regime i mod 4 with parameters
+    drawn from default_rng(seed): 0 a sinusoid, 1 an AR(1) process, 2 a square
+    wave, 3 a damped oscillation restarted every period.  The scalar series s
+    (length seqlen + 1, unit-scale) is embedded along one fixed random unit vector
+    u: X[i, t] = s_t u and the next-step target Y[i, t] = s_{t+1} u.  Returns
+    (X, Y), both float32 [n_seq, seqlen, d_model]."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(d_model).astype(np.float64)
+    u /= np.linalg.norm(u)
+    t = np.arange(seqlen + 1, dtype=np.float64)
+    S = np.empty((n_seq, seqlen + 1))
+    for i in range(n_seq):
+        r = i % 4
+        w = rng.uniform(0.05, 0.3)
+        ph = rng.uniform(0.0, 2.0 * math.pi)
+        if r == 0:
+            S[i] = np.sin(w * t + ph)
+        elif r == 1:
+            e = rng.standard_normal(seqlen + 1)
+            s = np.empty(seqlen + 1)
+            s[0] = e[0]
+            for k in range(1, seqlen + 1):
+                s[k] = 0.95 * s[k - 1] + 0.3 * e[k]
+            S[i] = s / max(np.max(np.abs(s)), 1e-9)
+        elif r == 2:
+            S[i] = 0.8 * np.sign(np.sin(w * t + ph))
+        else:
+            period = int(rng.integers(16, 48))
+            S[i] = np.exp(-0.05 * (t % period)) * np.cos(w * t + ph)
+    X = (S[:, :-1, None] * u).astype(np.float32)
+    Y = (S[:, 1:, None] * u).astype(np.float32)
+    return X, Y
