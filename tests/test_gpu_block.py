@@ -77,6 +77,15 @@ def test_block_f32_ragged_rank_and_chunked_scan(ctx):
     _check(ctx, X, p, dY, torch.float32, F32_TOL)
 
 
+@pytest.mark.parametrize("shape", [(1, 1, 8, 8, 1, 1), (3, 2, 16, 24, 2, 3), (2, 5, 8, 16, 40, 2)])
+def test_block_f32_edge_shapes(ctx, shape):
+    # one token; fewer tokens than the conv window; dt_rank larger than d_inner
+    b, L, dm, di, r, k = shape
+    X, p, dY = W.make_block_inputs(b, L, dm, di, 16, r, k, seed=60 + L)
+    p["conv_b"] = (0.2 * np.random.default_rng(L).standard_normal(di)).astype(np.float32)
+    _check(ctx, X, p, dY, torch.float32, F32_TOL)
+
+
 def test_block_bf16(ctx):
     X, p, dY = W.make_block_inputs(2, 256, 128, 256, 16, 8, 4, seed=54, bf16=True)
     print("bf16 block errors", _check(ctx, X, p, dY, torch.bfloat16, BF16_TOL))
