@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--cpu-sample-channels", type=int, default=0,
                     help="channels the oracle baseline runs on (0 = all)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
-    ap.add_argument("--op", choices=("scan", "conv1d", "decode", "block", "train"), default="scan",
+    ap.add_argument("--op", choices=("scan", "conv1d", "decode", "block", "train", "gdn2"), default="scan",
                     help="scan: the selective scan fwd+bwd (default); conv1d: the causal depthwise "
                          "conv1d + SiLU fwd+bwd in front of it, on the same batch/seqlen/d_inner; "
                          "decode: 1024 single-token steps at batch 256 x d_inner 5120, eager and "
@@ -529,6 +529,83 @@ def train_bench(args):
             f.write(out + "\n")
 
 
+def gdn2_bench(args):
+    """Gated DeltaNet-2 forward over batch 4 x 16 heads x 4096 tokens, k_dim =
+    v_dim = 128, f32 (inputs resident on the GPU)."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import selective_state_space_04_amd as ssm
+    import workloads as W
+
+    name = "gdn2_b4h16t4096"
+    c = W.GDN2_CONFIGS[name]
+    B, H, L, K, V = c["batch"], c["heads"], c["seqlen"], c["k_dim"], c["v_dim"]
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
+    inp = W.make_gdn2_config(name)
+    names = ("q", "k", "v", "g", "b", "w")
+    t = {n: torch.from_numpy(inp[n]).to(dev) for n in names}
+    scale = 1.0 / math.sqrt(K)
+    o = torch.empty(B, H, L, V, dtype=torch.float32, device=dev)
+
+    def step(timer=None):
+        ssm.ssm_gdn2_fwd(*[t[n] for n in names], None, scale=scale, o=o, timing=timer)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [ssm.LaunchTimer() for _ in range(args.steps)]
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(timers[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kms = float(np.mean([km for tm in timers for _, km in tm.results()]))
+    for tm in timers:
+        tm.close()
+    ht = B * H * L                       # head-tokens
+    flops = 7.0 * K * V * ht             # decay mul, erase-read, write and output FMAs per state element
+    nbytes = 4.0 * (4 * K + 3 * V) * ht  # q, k, g, b read; v, w read; o written (f32)
+    tflops = flops / (kms * 1e-3) / 1e12
+    line = {
+        "metric": "GDN2 forward tokens/s", "value": B * L / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{name}: batch={B} heads={H} seqlen={L} k_dim={K} v_dim={V}, f32, forward "
+                               f"(gated delta rule, token-by-token recurrence)",
+                   "batch": B, "heads": H, "seqlen": L, "k_dim": K, "v_dim": V},
+        "kernels_ms": {"k_gdn2_fwd": round(kms, 4)},
+        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": F32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / F32_VECTOR_PEAK_TFLOPS, 4), "traffic": None, "kernel": "k_gdn2_fwd"},
+        "roofline_hbm": {"bound": "hbm", "achieved": round(nbytes / (kms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(nbytes / (kms * 1e-3) / 8e12, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle import gdn2
+        Ls = 1024
+        sub = [inp[n][:1, :1, :Ls] for n in names]
+        t0 = time.perf_counter()
+        gdn2.recurrent(*sub, None, scale)
+        sec = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": Ls / H / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
+                                "kind": "oracle",
+                                "sample": f"batch 0, head 0, the first {Ls} tokens in f64 ({sec:.1f} s), scaled "
+                                          f"to all {H} heads of a token"}
+    out = json.dumps(line)
+    print(out, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(out + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -546,6 +623,9 @@ def main():
         return
     if args.op == "train":
         train_bench(args)
+        return
+    if args.op == "gdn2":
+        gdn2_bench(args)
         return
 
     import numpy as np

@@ -1,0 +1,56 @@
+/*
+ * ssm_gdn2.h -- C ABI (in libssmscan.so) of the Gated DeltaNet-2 forward on one
+ * MI355X (gfx950): a gated delta rule with a decay per key dimension and
+ * separate erase and write gates.
+ *
+ * Source of the operation: burn-gdn2 0.1.4, page "src/forward.rs": the chunked
+ * WY forward and its check against a sequential reference.  The page prints the
+ * chunk form only; the per-token recurrence that this form regroups exactly
+ * (with the decays kept per key dimension) is, for a [K, V] state S,
+ *     S'   = diag(exp(g_t)) S_{t-1}
+ *     vn_t = w_t * v_t - S'^T (b_t * k_t)
+ *     S_t  = S' + k_t vn_t^T
+ *     o_t  = scale * S_t^T q_t
+ * and that recurrence is what this call computes (the page's average of the
+ * decays over the key dimension, an approximation, is not reproduced).
+ *
+ * Conventions (as in ssm_scan.h): DEVICE pointers, dense row-major, 16-byte
+ * aligned, caller-owned; arguments are checked on the host before any launch;
+ * work is ordered on `stream`; nothing is allocated.
+ *   - q, k, g, b : [batch, heads, seqlen, k_dim] f32 (g: log-decays, normally <= 0)
+ *   - v, w, o    : [batch, heads, seqlen, v_dim] f32
+ *   - S0, S_last : [batch, heads, k_dim, v_dim] f32; S0 NULL = zero state;
+ *                  S_last NULL = not written; S_last may not alias S0.
+ *   - Limits: k_dim in {16, 32, 64, 128}; batch, heads <= 65535; io_dtype
+ *     SSM_F32 (SSM_BF16 returns SSM_E_UNSUPPORTED).  seqlen 0 writes S_last = S0.
+ */
+#ifndef SSM_GDN2_H
+#define SSM_GDN2_H
+
+#include "ssm_scan.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int64_t batch;
+    int64_t heads;
+    int64_t seqlen;
+    int64_t k_dim;
+    int64_t v_dim;
+    int32_t io_dtype; /* ssm_dtype */
+} ssm_gdn2_dims;
+
+/* Forward over the whole sequence from S0: writes o and, if non-NULL, S_last.
+ * Chaining calls through S_last -> S0 reproduces one call over the joined
+ * sequence bit for bit. */
+ssm_status ssm_gdn2_fwd(const ssm_gdn2_dims *dims, const float *q, const float *k, const float *v,
+                        const float *g, const float *b, const float *w, const float *S0, float scale,
+                        float *o, float *S_last, hipStream_t stream, ssm_timing *timing);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_GDN2_H */

@@ -69,7 +69,7 @@ typedef enum {
     SSM_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     SSM_E_WORKSPACE = 5,   /* workspace smaller than the query function returns */
     SSM_E_LAUNCH = 6,      /* a kernel launch failed (hipGetLastError) */
-    SSM_E_UNSUPPORTED = 7  /* valid but unsupported (d_state != 16, d_conv > 4, batch > 65535) */
+    SSM_E_UNSUPPORTED = 7  /* valid but outside the limits a header states (d_state != 16, ...) */
 } ssm_status;
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -114,7 +114,8 @@ enum {
     SSM_K_CONV_BWD_REDUCE = 13, /* fixed-order sum of dw/dbias partials */
     SSM_K_CONV_STEP = 14,    /* one token through the conv ring */
     SSM_K_CONV_RING = 15,    /* ring copies/fills when seqlen == 0 */
-    SSM_K_BLOCK_BC = 16      /* x_proj's B/C columns split / joined (ssm_block.h) */
+    SSM_K_BLOCK_BC = 16,     /* x_proj's B/C columns split / joined (ssm_block.h) */
+    SSM_K_GDN2_FWD = 17      /* Gated DeltaNet-2 forward recurrence (ssm_gdn2.h) */
 };
 
 /* Name of a kernel id (for matching profiler output); "?" if unknown. */

@@ -41,6 +41,11 @@ class ConvDims(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32)]
 
 
+class Gdn2Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("k_dim", ctypes.c_int64), ("v_dim", ctypes.c_int64), ("io_dtype", ctypes.c_int32)]
+
+
 class SsmTiming(ctypes.Structure):
     _fields_ = [("events", ctypes.c_void_p), ("capacity", ctypes.c_int32),
                 ("count", ctypes.c_int32), ("kernel_id", ctypes.c_int32 * TIMING_MAX)]
@@ -83,6 +88,8 @@ def _load_library():
     lib.ssm_conv1d_bwd.restype = ctypes.c_int
     lib.ssm_conv1d_step.argtypes = [I64, I64, I64, I32] + [P] * 5 + [P, TP]
     lib.ssm_conv1d_step.restype = ctypes.c_int
+    lib.ssm_gdn2_fwd.argtypes = [ctypes.POINTER(Gdn2Dims)] + [P] * 7 + [ctypes.c_float, P, P, P, TP]
+    lib.ssm_gdn2_fwd.restype = ctypes.c_int
     return lib
 
 
@@ -303,6 +310,31 @@ def ssm_conv1d_fwd(x, w, bias=None, ring0=None, *, return_ring=False, y=None, st
                              _ptr(ring_last), _stream(dev, stream), _timing_ptr(timing))
     _raise("ssm_conv1d_fwd", rc)
     return y, ring_last
+
+
+def ssm_gdn2_fwd(q, k, v, g, b, w, S0=None, *, scale=1.0, return_state=True, o=None, stream=None,
+                 timing=None):
+    """Gated DeltaNet-2 forward (the gated delta rule with per-key-dimension decay,
+    token by token).  q, k, g, b [batch, heads, L, k_dim] and v, w [batch, heads, L,
+    v_dim] float32; S0 [batch, heads, k_dim, v_dim] float32 or None (zeros).
+    Returns (o [batch, heads, L, v_dim], S_last or None)."""
+    dev = q.device
+    bsz, nh, L, kd = q.shape
+    vd = v.shape[-1] if v.dim() == 4 else -1
+    for t, n in ((q, "q"), (k, "k"), (g, "g"), (b, "b")):
+        _check(t, n, (bsz, nh, L, kd), torch.float32, dev)
+    for t, n in ((v, "v"), (w, "w")):
+        _check(t, n, (bsz, nh, L, vd), torch.float32, dev)
+    _check(S0, "S0", (bsz, nh, kd, vd), torch.float32, dev, required=False)
+    if o is None:
+        o = torch.empty(bsz, nh, L, vd, dtype=torch.float32, device=dev)
+    _check(o, "o", (bsz, nh, L, vd), torch.float32, dev)
+    S_last = torch.empty(bsz, nh, kd, vd, dtype=torch.float32, device=dev) if return_state else None
+    dm = Gdn2Dims(bsz, nh, L, kd, vd, 0)
+    rc = _lib.ssm_gdn2_fwd(ctypes.byref(dm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(S0),
+                           float(scale), _ptr(o), _ptr(S_last), _stream(dev, stream), _timing_ptr(timing))
+    _raise("ssm_gdn2_fwd", rc)
+    return o, S_last
 
 
 def ssm_conv1d_bwd(x, w, bias, dy, ring0=None, *, want_dring0=False, stream=None, timing=None, out=None):
@@ -544,4 +576,4 @@ __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_scan_step", "ckpt_bytes", "fwd_w
            "bwd_workspace_bytes", "LaunchTimer", "SsmError", "library", "status_str", "kernel_name",
            "SsmDims", "SsmTiming", "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_conv1d_step",
            "conv1d_bwd_workspace_bytes", "ConvDims", "BlockContext", "ssm_block_fwd", "ssm_block_bwd",
-           "block_library", "BlockDims"]
+           "block_library", "BlockDims", "ssm_gdn2_fwd", "Gdn2Dims"]

@@ -1,12 +1,12 @@
-"""Compiles libssmscan.so (HIP, gfx950 only: the selective scan and the conv1d
-in front of it) and libssmblock.so (one Mamba block: those kernels plus the
+"""Compiles libssmscan.so (HIP, gfx950 only: the selective scan, the conv1d in
+front of it and the Gated DeltaNet-2 forward) and libssmblock.so (one Mamba block: those kernels plus the
 projections on hipBLASLt) in-tree with hipcc."""
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", "ssm_scan.hip"), os.path.join(HERE, "csrc", "ssm_conv1d.hip")]
+SRCS = [os.path.join(HERE, "csrc", n) for n in ("ssm_scan.hip", "ssm_conv1d.hip", "ssm_gdn2.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libssmscan.so")
 BLOCK_SRC = os.path.join(HERE, "csrc", "ssm_block.hip")

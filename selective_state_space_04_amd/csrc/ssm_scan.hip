@@ -937,7 +937,8 @@ const char* ssm_status_str(ssm_status s) {
         case SSM_E_WORKSPACE: return "workspace too small";
         case SSM_E_LAUNCH: return "kernel launch failed";
         case SSM_E_UNSUPPORTED:
-            return "unsupported configuration (d_state must be 16, d_conv 1..4, batch <= 65535)";
+            return "unsupported configuration (outside the limits its header states: e.g. d_state 16, "
+                   "d_conv 1..4, batch <= 65535, GDN2 k_dim 16/32/64/128 in f32)";
     }
     return "unknown status";
 }
@@ -960,6 +961,7 @@ const char* ssm_kernel_name(int32_t id) {
         case SSM_K_CONV_STEP: return "k_conv_step";
         case SSM_K_CONV_RING: return "k_conv_ring";
         case SSM_K_BLOCK_BC: return "k_block_bc";
+        case SSM_K_GDN2_FWD: return "k_gdn2_fwd";
     }
     return "?";
 }

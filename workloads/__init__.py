@@ -222,3 +222,40 @@ def make_regime_corpus(n_seq, seqlen, d_model, *, seed=0):
     X = (S[:, :-1, None] * u).astype(np.float32)
     Y = (S[:, 1:, None] * u).astype(np.float32)
     return X, Y
+
+
+GDN2_CONFIGS = {
+    # name: batch, heads, seqlen, k_dim, v_dim (f32)
+    "gdn2_b4h16t4096": dict(batch=4, heads=16, seqlen=4096, k_dim=128, v_dim=128),
+}
+
+
+def make_gdn2_inputs(batch, heads, seqlen, k_dim, v_dim, *, seed=0, with_state=False):
+    """Gated DeltaNet-2 forward inputs.  Draw order from default_rng(seed), each
+    standard_normal(float32) of its shape: q, k [B, H, L, K], v [B, H, L, V], then
+    g_raw, b_raw [B, H, L, K], w_raw [B, H, L, V], then S0 [B, H, K, V] if asked.
+    Shaping: k is scaled to unit L2 norm per token (the usual key normalisation of
+    delta rules); g = -exp(0.5 g_raw - 3) (log-decays, decay factors exp(g) mostly
+    0.9 .. 1); b = sigmoid(b_raw) and w = sigmoid(w_raw) (gates in (0, 1)); S0 is
+    scaled by 0.1.  The scale 1/sqrt(K) is the caller's."""
+    rng = np.random.default_rng(seed)
+    shk, shv = (batch, heads, seqlen, k_dim), (batch, heads, seqlen, v_dim)
+    q = rng.standard_normal(shk, dtype=np.float32)
+    k = rng.standard_normal(shk, dtype=np.float32)
+    v = rng.standard_normal(shv, dtype=np.float32)
+    g_raw = rng.standard_normal(shk, dtype=np.float32)
+    b_raw = rng.standard_normal(shk, dtype=np.float32)
+    w_raw = rng.standard_normal(shv, dtype=np.float32)
+    k = (k / np.maximum(np.linalg.norm(k, axis=-1, keepdims=True), 1e-6)).astype(np.float32)
+    g = (-np.exp(0.5 * g_raw - 3.0)).astype(np.float32)
+    b = (1.0 / (1.0 + np.exp(-b_raw))).astype(np.float32)
+    w = (1.0 / (1.0 + np.exp(-w_raw))).astype(np.float32)
+    out = {"q": q, "k": k, "v": v, "g": g, "b": b, "w": w, "S0": None}
+    if with_state:
+        out["S0"] = (0.1 * rng.standard_normal((batch, heads, k_dim, v_dim), dtype=np.float32)).astype(np.float32)
+    return out
+
+
+def make_gdn2_config(name, *, seed=0):
+    c = GDN2_CONFIGS[name]
+    return make_gdn2_inputs(c["batch"], c["heads"], c["seqlen"], c["k_dim"], c["v_dim"], seed=seed)
