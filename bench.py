@@ -61,7 +61,8 @@ def parse():
     ap.add_argument("--cpu-sample-channels", type=int, default=0,
                     help="channels the oracle baseline runs on (0 = all)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
-    ap.add_argument("--op", choices=("scan", "conv1d", "decode", "block", "train", "gdn2"), default="scan",
+    ap.add_argument("--op", choices=("scan", "conv1d", "decode", "block", "block-c", "train", "gdn2"),
+                    default="scan",
                     help="scan: the selective scan fwd+bwd (default); conv1d: the causal depthwise "
                          "conv1d + SiLU fwd+bwd in front of it, on the same batch/seqlen/d_inner; "
                          "decode: 1024 single-token steps at batch 256 x d_inner 5120, eager and "
@@ -606,6 +607,43 @@ def gdn2_bench(args):
             f.write(out + "\n")
 
 
+def block_c_bench(args):
+    """The block_mamba2p8b_bf16 workload (fwd+bwd) timed by tests/c_abi/block_from_c,
+    a C++ program that calls libssmblock.so with no PyTorch in its process, so the
+    projections run on the system ROCm hipBLASLt.  Its inputs are uniform random
+    values of the same shapes and scales (its own generator)."""
+    import subprocess
+
+    import workloads as W
+
+    exe = os.path.join(ROOT, "tests", "c_abi", "block_from_c")
+    if not os.path.exists(exe):
+        raise SystemExit(f"{exe} is missing: build the package first")
+    res = subprocess.run([exe, "time", str(args.steps), str(args.warmup)], capture_output=True, text=True,
+                         timeout=600)
+    if res.returncode != 0:
+        raise SystemExit(f"block_from_c failed ({res.returncode}): {res.stdout}{res.stderr}")
+    ms = float(res.stdout.split()[-1])
+    cfg = W.BLOCK_CONFIGS["block_mamba2p8b_bf16"]
+    B, L = cfg["batch"], cfg["seqlen"]
+    line = {
+        "metric": "Mamba block fwd+bwd tokens/s (C caller, system ROCm libraries)",
+        "value": B * L / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"block_mamba2p8b_bf16: batch={B} seqlen={L} d_model={cfg['d_model']} "
+                               f"d_inner={cfg['d_inner']} d_state=16 dt_rank={cfg['dt_rank']} d_conv=4, bf16, "
+                               f"fwd+bwd, driven from a C++ program",
+                   "batch": B, "seqlen": L, "d_model": cfg["d_model"], "d_inner": cfg["d_inner"]},
+        "cpu_baseline": None,
+    }
+    out = json.dumps(line)
+    print(out, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(out + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -623,6 +661,9 @@ def main():
         return
     if args.op == "train":
         train_bench(args)
+        return
+    if args.op == "block-c":
+        block_c_bench(args)
         return
     if args.op == "gdn2":
         gdn2_bench(args)

@@ -38,19 +38,20 @@ def _hipcc(cmd, out, verbose):
     os.replace(tmp, out)
 
 
-C_DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi", "scan_from_c.cpp")
-C_DRIVER = os.path.join(ROOT, "tests", "c_abi", "scan_from_c")
+C_DRIVERS = [(os.path.join(ROOT, "tests", "c_abi", n + ".cpp"), os.path.join(ROOT, "tests", "c_abi", n), lib)
+             for n, lib in (("scan_from_c", ["-lssmscan"]), ("block_from_c", ["-lssmblock", "-lssmscan"]))]
 
 
 def build(verbose=False, extra=()):
     """libssmscan.so (scan, conv1d and GDN2 kernels), then libssmblock.so (the
-    Mamba block on top of it and hipBLASLt), then the host-only test program that
-    drives libssmscan.so through its C ABI."""
+    Mamba block on top of it and hipBLASLt), then the host-only test programs that
+    drive the two libraries through their C ABI."""
     _hipcc([HIPCC, *FLAGS, *extra, "-I", INCLUDE, *SRCS], LIB_PATH, verbose)
     _hipcc([HIPCC, *FLAGS, *extra, "-I", INCLUDE, BLOCK_SRC, "-L", HERE, "-lssmscan",
             f"-L{ROCM_LIB}", "-lhipblaslt", "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{ROCM_LIB}"],
            BLOCK_LIB_PATH, verbose)
-    _hipcc([HIPCC, "-O2", "-std=c++17", "-Wall", "-I", INCLUDE, C_DRIVER_SRC, "-L", HERE, "-lssmscan",
-            "-Wl,-rpath,$ORIGIN/../../selective_state_space_04_amd", f"-Wl,-rpath,{ROCM_LIB}"],
-           C_DRIVER, verbose)
+    for src, out, lib in C_DRIVERS:
+        _hipcc([HIPCC, "-O2", "-std=c++17", "-Wall", "-I", INCLUDE, src, "-L", HERE, *lib,
+                "-Wl,-rpath,$ORIGIN/../../selective_state_space_04_amd", f"-Wl,-rpath,{ROCM_LIB}"],
+               out, verbose)
     return LIB_PATH

@@ -56,3 +56,37 @@ def test_scan_from_a_c_program(tmp_path, shape):
     assert _rel(r["y"], ref["y"]) <= 1e-5 and _rel(r["h_last"], ref["h_last"]) <= 1e-5
     for n in ("dx", "ddt", "dz", "dB", "dC", "dA_log", "dD", "ddt_bias"):
         assert _rel(r[n], gref[n]) <= 1e-4, (n, _rel(r[n], gref[n]))
+
+
+BLOCK_DRIVER = os.path.join(ROOT, "tests", "c_abi", "block_from_c")
+
+
+def test_block_from_a_c_program(tmp_path):
+    """One f32 Mamba block (batch 2 x 100 tokens, d_model 64, d_inner 128) through
+    libssmblock.so from a C++ program, so its GEMMs run on the system ROCm
+    hipBLASLt; every output against the f64 block oracle at 1e-4."""
+    from oracle.block import PARAMS, block_bwd, block_fwd
+
+    assert os.path.exists(BLOCK_DRIVER), "build the package first (it compiles tests/c_abi/block_from_c)"
+    out = str(tmp_path / "block.bin")
+    res = subprocess.run([BLOCK_DRIVER, "check", out], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    with open(out, "rb") as f:
+        Bt, L, dm, di, N, R, K = (int(v) for v in np.frombuffer(f.read(56), dtype=np.int64))
+        P = R + 2 * N
+
+        def take(*shape):
+            n = int(np.prod(shape))
+            return np.frombuffer(f.read(4 * n), dtype=np.float32).reshape(shape).astype(np.float64)
+
+        X, dY = take(Bt, L, dm), take(Bt, L, dm)
+        p = {"W_in": take(2 * di, dm), "conv_w": take(di, K), "conv_b": take(di), "W_x": take(P, di),
+             "W_dt": take(di, R), "dt_bias": take(di), "A_log": take(di, N), "D": take(di), "W_out": take(dm, di)}
+        got = {"Y": take(Bt, L, dm), "dX": take(Bt, L, dm)}
+        for n in PARAMS:
+            got["d" + n] = take(*p[n].shape)
+        assert not f.read(1), "trailing bytes"
+    ref, gr = block_fwd(X, p), block_bwd(X, p, dY)
+    errs = {"Y": _rel(got["Y"], ref["Y"]), "dX": _rel(got["dX"], gr["dX"])}
+    errs.update({"d" + n: _rel(got["d" + n], gr["d" + n]) for n in PARAMS})
+    assert all(v <= 1e-4 for v in errs.values()), errs
