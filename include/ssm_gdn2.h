@@ -17,12 +17,14 @@
  * Conventions (as in ssm_scan.h): DEVICE pointers, dense row-major, 16-byte
  * aligned, caller-owned; arguments are checked on the host before any launch;
  * work is ordered on `stream`; nothing is allocated.
- *   - q, k, g, b : [batch, heads, seqlen, k_dim] f32 (g: log-decays, normally <= 0)
- *   - v, w, o    : [batch, heads, seqlen, v_dim] f32
+ *   - q, k, g, b : [batch, heads, seqlen, k_dim] io dtype (g: log-decays, normally <= 0)
+ *   - v, w, o    : [batch, heads, seqlen, v_dim] io dtype
+ *   - io dtype SSM_F32, or SSM_BF16 (values read as bf16, arithmetic and state in
+ *     f32, o rounded to nearest even)
  *   - S0, S_last : [batch, heads, k_dim, v_dim] f32; S0 NULL = zero state;
  *                  S_last NULL = not written; S_last may not alias S0.
- *   - Limits: k_dim in {16, 32, 64, 128}; batch, heads <= 65535; io_dtype
- *     SSM_F32 (SSM_BF16 returns SSM_E_UNSUPPORTED).  seqlen 0 writes S_last = S0.
+ *   - Limits: k_dim in {16, 32, 64, 128}; batch, heads <= 65535.  seqlen 0 writes
+ *     S_last = S0 (zeros when S0 is NULL).
  */
 #ifndef SSM_GDN2_H
 #define SSM_GDN2_H
@@ -45,9 +47,9 @@ typedef struct {
 /* Forward over the whole sequence from S0: writes o and, if non-NULL, S_last.
  * Chaining calls through S_last -> S0 reproduces one call over the joined
  * sequence bit for bit. */
-ssm_status ssm_gdn2_fwd(const ssm_gdn2_dims *dims, const float *q, const float *k, const float *v,
-                        const float *g, const float *b, const float *w, const float *S0, float scale,
-                        float *o, float *S_last, hipStream_t stream, ssm_timing *timing);
+ssm_status ssm_gdn2_fwd(const ssm_gdn2_dims *dims, const void *q, const void *k, const void *v,
+                        const void *g, const void *b, const void *w, const float *S0, float scale,
+                        void *o, float *S_last, hipStream_t stream, ssm_timing *timing);
 
 #ifdef __cplusplus
 }

@@ -316,21 +316,23 @@ def ssm_gdn2_fwd(q, k, v, g, b, w, S0=None, *, scale=1.0, return_state=True, o=N
                  timing=None):
     """Gated DeltaNet-2 forward (the gated delta rule with per-key-dimension decay,
     token by token).  q, k, g, b [batch, heads, L, k_dim] and v, w [batch, heads, L,
-    v_dim] float32; S0 [batch, heads, k_dim, v_dim] float32 or None (zeros).
-    Returns (o [batch, heads, L, v_dim], S_last or None)."""
+    v_dim], all float32 or all bfloat16 (state and arithmetic f32 either way);
+    S0 [batch, heads, k_dim, v_dim] float32 or None (zeros).  Returns
+    (o [batch, heads, L, v_dim] in the activations' dtype, S_last float32 or None)."""
     dev = q.device
+    io = q.dtype
     bsz, nh, L, kd = q.shape
     vd = v.shape[-1] if v.dim() == 4 else -1
     for t, n in ((q, "q"), (k, "k"), (g, "g"), (b, "b")):
-        _check(t, n, (bsz, nh, L, kd), torch.float32, dev)
+        _check(t, n, (bsz, nh, L, kd), io, dev)
     for t, n in ((v, "v"), (w, "w")):
-        _check(t, n, (bsz, nh, L, vd), torch.float32, dev)
+        _check(t, n, (bsz, nh, L, vd), io, dev)
     _check(S0, "S0", (bsz, nh, kd, vd), torch.float32, dev, required=False)
     if o is None:
-        o = torch.empty(bsz, nh, L, vd, dtype=torch.float32, device=dev)
-    _check(o, "o", (bsz, nh, L, vd), torch.float32, dev)
+        o = torch.empty(bsz, nh, L, vd, dtype=io, device=dev)
+    _check(o, "o", (bsz, nh, L, vd), io, dev)
     S_last = torch.empty(bsz, nh, kd, vd, dtype=torch.float32, device=dev) if return_state else None
-    dm = Gdn2Dims(bsz, nh, L, kd, vd, 0)
+    dm = Gdn2Dims(bsz, nh, L, kd, vd, _io_code(io))
     rc = _lib.ssm_gdn2_fwd(ctypes.byref(dm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(S0),
                            float(scale), _ptr(o), _ptr(S_last), _stream(dev, stream), _timing_ptr(timing))
     _raise("ssm_gdn2_fwd", rc)

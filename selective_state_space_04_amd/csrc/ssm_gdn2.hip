@@ -49,6 +49,14 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// Four consecutive activations of type T as floats (T = float or bf16 bits).
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const ssm::bf16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 // Tokens per chunk staged through LDS: the key-side vectors of a chunk (q, k,
 // exp(g) and b * k, K floats each per token) and w * v for the workgroup's
 // columns are loaded by the whole workgroup while the previous chunk is being
@@ -56,11 +64,11 @@ __device__ __forceinline__ float row_sum16(float x) {
 // column keeps the output of token r of the chunk and stores it at the end.
 constexpr int TC = ROWS;
 
-template <int R>
+template <typename TT, int R>
 __global__ __launch_bounds__(WG) void k_gdn2_fwd(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ b, const float* __restrict__ w,
-    const float* __restrict__ S0, float scale, float* __restrict__ o, float* __restrict__ S_last,
+    const TT* __restrict__ q, const TT* __restrict__ k, const TT* __restrict__ v,
+    const TT* __restrict__ g, const TT* __restrict__ b, const TT* __restrict__ w,
+    const float* __restrict__ S0, float scale, TT* __restrict__ o, float* __restrict__ S_last,
     int H, int T, int V) {
     constexpr int K = ROWS * R;
     constexpr int K4 = K / 4 > 0 ? K / 4 : 1;          // float4 pieces per token row (K >= 16)
@@ -75,10 +83,10 @@ __global__ __launch_bounds__(WG) void k_gdn2_fwd(
     const bool act = j < V;
     const int jc = act ? j : V - 1;
     const int64_t bh = (int64_t)blockIdx.z * H + blockIdx.y;
-    const float* qb = q + bh * T * K;
-    const float* kb = k + bh * T * K;
-    const float* gb = g + bh * T * K;
-    const float* bb = b + bh * T * K;
+    const TT* qb = q + bh * T * K;
+    const TT* kb = k + bh * T * K;
+    const TT* gb = g + bh * T * K;
+    const TT* bb = b + bh * T * K;
     float S[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) S[i] = S0 ? S0[(bh * K + R * r + i) * V + jc] : 0.0f;
@@ -94,17 +102,17 @@ __global__ __launch_bounds__(WG) void k_gdn2_fwd(
             const int idx = tid + s2 * WG;
             if (idx < nt * K4) {
                 const int64_t off = (int64_t)t0 * K + (int64_t)idx * 4;
-                rq[s2] = *reinterpret_cast<const float4*>(qb + off);
-                rk[s2] = *reinterpret_cast<const float4*>(kb + off);
-                rg[s2] = *reinterpret_cast<const float4*>(gb + off);
-                rb[s2] = *reinterpret_cast<const float4*>(bb + off);
+                rq[s2] = load4(qb + off);
+                rk[s2] = load4(kb + off);
+                rg[s2] = load4(gb + off);
+                rb[s2] = load4(bb + off);
             }
         }
         const int tt = tid / CPB, col = j0 + tid % CPB;
         rwv = 0.0f;
         if (tt < nt && col < V) {
             const int64_t e = (bh * T + t0 + tt) * V + col;
-            rwv = w[e] * v[e];
+            rwv = ssm::to_f(w[e]) * ssm::to_f(v[e]);
         }
     };
     auto stage_store = [&](int c, int buf) {
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(WG) void k_gdn2_fwd(
         } else {
             for (int tt = 0; tt < nt; ++tt) token(tt);
         }
-        if (act && r < nt) o[(bh * T + t0 + r) * V + j] = scale * mine;
+        if (act && r < nt) o[(bh * T + t0 + r) * V + j] = ssm::from_f<TT>(scale * mine);
         if (c + 1 < nch) stage_store(c + 1, buf ^ 1);
         __syncthreads();
     }
@@ -179,7 +187,6 @@ ssm_status check_gdn2(const ssm_gdn2_dims* d) {
     if (!d) return SSM_E_NULLPTR;
     if (d->batch < 1 || d->heads < 1 || d->seqlen < 0 || d->k_dim < 1 || d->v_dim < 1) return SSM_E_SHAPE;
     if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_E_DTYPE;
-    if (d->io_dtype != SSM_F32) return SSM_E_UNSUPPORTED;
     if (d->k_dim != 16 && d->k_dim != 32 && d->k_dim != 64 && d->k_dim != 128) return SSM_E_UNSUPPORTED;
     if (d->batch > 65535 || d->heads > 65535 || d->seqlen > ((int64_t)1 << 30) ||
         d->v_dim > ((int64_t)1 << 30))
@@ -187,22 +194,35 @@ ssm_status check_gdn2(const ssm_gdn2_dims* d) {
     return SSM_OK;
 }
 
-template <int R>
-ssm_status run(const ssm_gdn2_dims* d, const float* q, const float* k, const float* v, const float* g,
-               const float* b, const float* w, const float* S0, float scale, float* o, float* S_last,
+template <typename TT, int R>
+ssm_status run(const ssm_gdn2_dims* d, const void* q, const void* k, const void* v, const void* g,
+               const void* b, const void* w, const float* S0, float scale, void* o, float* S_last,
                ssm::Launcher& launch) {
     const dim3 grid((unsigned)((d->v_dim + CPB - 1) / CPB), (unsigned)d->heads, (unsigned)d->batch);
-    return launch(SSM_K_GDN2_FWD, k_gdn2_fwd<R>, grid, dim3(WG), q, k, v, g, b, w, S0, scale, o, S_last,
-                  (int)d->heads, (int)d->seqlen, (int)d->v_dim);
+    return launch(SSM_K_GDN2_FWD, k_gdn2_fwd<TT, R>, grid, dim3(WG), (const TT*)q, (const TT*)k, (const TT*)v,
+                  (const TT*)g, (const TT*)b, (const TT*)w, S0, scale, (TT*)o, S_last, (int)d->heads,
+                  (int)d->seqlen, (int)d->v_dim);
+}
+
+template <typename TT>
+ssm_status run_k(const ssm_gdn2_dims* d, const void* q, const void* k, const void* v, const void* g,
+                 const void* b, const void* w, const float* S0, float scale, void* o, float* S_last,
+                 ssm::Launcher& launch) {
+    switch (d->k_dim) {
+        case 16: return run<TT, 1>(d, q, k, v, g, b, w, S0, scale, o, S_last, launch);
+        case 32: return run<TT, 2>(d, q, k, v, g, b, w, S0, scale, o, S_last, launch);
+        case 64: return run<TT, 4>(d, q, k, v, g, b, w, S0, scale, o, S_last, launch);
+        default: return run<TT, 8>(d, q, k, v, g, b, w, S0, scale, o, S_last, launch);
+    }
 }
 
 }  // namespace
 
 extern "C" {
 
-ssm_status ssm_gdn2_fwd(const ssm_gdn2_dims* dims, const float* q, const float* k, const float* v,
-                        const float* g, const float* b, const float* w, const float* S0, float scale,
-                        float* o, float* S_last, hipStream_t stream, ssm_timing* timing) {
+ssm_status ssm_gdn2_fwd(const ssm_gdn2_dims* dims, const void* q, const void* k, const void* v,
+                        const void* g, const void* b, const void* w, const float* S0, float scale,
+                        void* o, float* S_last, hipStream_t stream, ssm_timing* timing) {
     SSM_TRY(check_gdn2(dims));
     if (dims->seqlen > 0 && (!q || !k || !v || !g || !b || !w || !o)) return SSM_E_NULLPTR;
     if (S_last && S_last == S0) return SSM_E_UNSUPPORTED;
@@ -212,12 +232,8 @@ ssm_status ssm_gdn2_fwd(const ssm_gdn2_dims* dims, const float* q, const float* 
     if (dims->seqlen == 0 && !S_last) return SSM_OK;
     (void)hipGetLastError();
     ssm::Launcher launch{stream, timing};
-    switch (dims->k_dim) {
-        case 16: return run<1>(dims, q, k, v, g, b, w, S0, scale, o, S_last, launch);
-        case 32: return run<2>(dims, q, k, v, g, b, w, S0, scale, o, S_last, launch);
-        case 64: return run<4>(dims, q, k, v, g, b, w, S0, scale, o, S_last, launch);
-        default: return run<8>(dims, q, k, v, g, b, w, S0, scale, o, S_last, launch);
-    }
+    if (dims->io_dtype == SSM_BF16) return run_k<ssm::bf16_t>(dims, q, k, v, g, b, w, S0, scale, o, S_last, launch);
+    return run_k<float>(dims, q, k, v, g, b, w, S0, scale, o, S_last, launch);
 }
 
 }  // extern "C"

@@ -333,7 +333,7 @@ def test_gdn2_rejects_bad_arguments():
     assert call(dims(L=-1)) == SHAPE
     assert call(dims(vd=0)) == SHAPE
     assert call(dims(io=7)) == DTYPE
-    assert call(dims(io=1)) == UNSUPPORTED          # bf16 not offered
+    assert call(dims(io=1), q=FAKE + 2) == ALIGN     # bf16 activations, misaligned
     assert call(dims(kd=48)) == UNSUPPORTED         # k_dim in {16, 32, 64, 128}
     assert call(dims(kd=256)) == UNSUPPORTED
     assert call(dims(h=70000)) == UNSUPPORTED

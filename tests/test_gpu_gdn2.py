@@ -98,3 +98,24 @@ def test_repeatable_and_empty():
     e["S0"] = None
     _, Sz = _run(e, 0.5)
     assert torch.count_nonzero(Sz) == 0
+
+
+@pytest.mark.parametrize("kd", [32, 128])
+def test_parity_bf16_activations(kd):
+    """bf16 activations (both sides use the rounded values), f32 state: the final
+    state to the f32 bound, the bf16 outputs to 2^-8 relative (their rounding)."""
+    inp = W.make_gdn2_inputs(2, 3, 200, kd, 40, seed=kd, with_state=True)
+    for n in NAMES:
+        inp[n] = W.round_bf16(inp[n])
+    t = {n: torch.from_numpy(inp[n]).to(DEV).to(torch.bfloat16) for n in NAMES}
+    t["S0"] = torch.from_numpy(inp["S0"]).to(DEV)
+    o, S = _run(t, 1.0 / math.sqrt(kd))
+    assert o.dtype == torch.bfloat16 and S.dtype == torch.float32
+    ro, rS = gdn2.recurrent(*[inp[n] for n in NAMES], inp["S0"], 1.0 / math.sqrt(kd))
+    assert _rel(S, rS) <= TOL
+    assert _rel(o, ro) <= 2 ** -8, _rel(o, ro)
+    # the bf16 path equals the f32 path on the same values, rounded once at the end
+    t32 = {n: t[n].float() for n in NAMES}
+    t32["S0"] = t["S0"]
+    o32, S32 = _run(t32, 1.0 / math.sqrt(kd))
+    assert torch.equal(S, S32) and torch.equal(o, o32.to(torch.bfloat16))
