@@ -119,3 +119,22 @@ def test_parity_bf16_activations(kd):
     t32["S0"] = t["S0"]
     o32, S32 = _run(t32, 1.0 / math.sqrt(kd))
     assert torch.equal(S, S32) and torch.equal(o, o32.to(torch.bfloat16))
+
+
+def test_extreme_gates():
+    """Decays of exactly 1 (g = 0) and of 0 to f32 precision (g = -200: the state
+    is wiped every token), erase and write gates at 0 and 1, unnormalised keys."""
+    inp = W.make_gdn2_inputs(1, 4, 64, 64, 24, seed=8, with_state=True)
+    g = inp["g"]
+    g[:, 0] = 0.0
+    g[:, 1] = -200.0
+    inp["b"][:, 2] = 1.0
+    inp["w"][:, 2] = 0.0
+    inp["b"][:, 3] = 0.0
+    inp["w"][:, 3] = 1.0
+    inp["k"][:, 3] *= 3.0
+    o, S = _run(_dev(inp), 0.25)
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    ro, rS = gdn2.recurrent(*[inp[n] for n in NAMES], inp["S0"], 0.25)
+    for h in range(4):
+        assert _rel(o[:, h], ro[:, h]) <= TOL and _rel(S[:, h], rS[:, h]) <= TOL, h
