@@ -37,7 +37,9 @@ TRAFFIC = {"scan": (os.path.join(CSRC, "ssm_scan.hip"),
            "conv1d": (os.path.join(CSRC, "ssm_conv1d.hip"),
                       os.path.join(ROOT, "profiles", "conv_mamba2p8b_bf16_traffic.txt")),
            "decode": (os.path.join(CSRC, "ssm_scan.hip"),
-                      os.path.join(ROOT, "profiles", "c5_decode_step_traffic.txt"))}
+                      os.path.join(ROOT, "profiles", "c5_decode_step_traffic.txt")),
+           "gdn2": (os.path.join(CSRC, "ssm_gdn2.hip"),
+                    os.path.join(ROOT, "profiles", "gdn2_b4h16t4096_traffic.txt"))}
 
 # Algorithmic f32 flops per element (b,t,d,n), FMA = 2, mul/add/exp = 1.
 #  forward main : exp(dt*A) (mul + exp), dt*x*B (mul), h update (FMA), C.h (FMA)  = 7
@@ -555,6 +557,8 @@ def gdn2_bench(args):
     def step(timer=None):
         ssm.ssm_gdn2_fwd(*[t[n] for n in names], None, scale=scale, o=o, timing=timer)
 
+    if args.copy_probe:
+        copy_probe(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -583,7 +587,8 @@ def gdn2_bench(args):
                    "batch": B, "heads": H, "seqlen": L, "k_dim": K, "v_dim": V},
         "kernels_ms": {"k_gdn2_fwd": round(kms, 4)},
         "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": F32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / F32_VECTOR_PEAK_TFLOPS, 4), "traffic": None, "kernel": "k_gdn2_fwd"},
+                     "frac": round(tflops / F32_VECTOR_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("k_gdn2_fwd", "gdn2"), "kernel": "k_gdn2_fwd"},
         "roofline_hbm": {"bound": "hbm", "achieved": round(nbytes / (kms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(nbytes / (kms * 1e-3) / 8e12, 4)},
         "cpu_baseline": None,

@@ -14,7 +14,9 @@
 //     the key dimension per token (the erase read and the output) are R
 //     in-lane FMAs and four DPP adds across the row, after which every lane of
 //     the row holds the total (fixed order: bitwise repeatable).
-//   * A wave is 4 columns, a workgroup 16.  The key-side vectors are staged in
+//   * A wave is 4 columns, a workgroup 16; the column blocks of one (batch,
+//     head) pair are numbered to run on one XCD so that its L2 serves their
+//     shared key-side reads.  The key-side vectors are staged in
 //     chunks of 16 tokens through double-buffered LDS (exp(g) and b * k formed
 //     once per element there), loaded while the previous chunk is computed.
 //   * No atomics, no MFMA: per token this form is rank-one updates and
@@ -31,6 +33,7 @@ namespace {
 constexpr int WG = 256;
 constexpr int ROWS = 16;            // lanes per column (one DPP row)
 constexpr int CPB = WG / ROWS;      // columns per workgroup
+constexpr int XCDS = 8;             // XCDs of an MI355X (one L2 each)
 constexpr float LOG2E = 1.4426950408889634f;
 
 template <int CTRL>
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(WG) void k_gdn2_fwd(
     const TT* __restrict__ q, const TT* __restrict__ k, const TT* __restrict__ v,
     const TT* __restrict__ g, const TT* __restrict__ b, const TT* __restrict__ w,
     const float* __restrict__ S0, float scale, TT* __restrict__ o, float* __restrict__ S_last,
-    int H, int T, int V) {
+    int64_t nbh, int ncb, int T, int V) {
     constexpr int K = ROWS * R;
     constexpr int K4 = K / 4 > 0 ? K / 4 : 1;          // float4 pieces per token row (K >= 16)
     constexpr int NST = (TC * K4 + WG - 1) / WG;       // float4 pieces per thread per vector
@@ -78,11 +81,18 @@ __global__ __launch_bounds__(WG) void k_gdn2_fwd(
     const int tid = threadIdx.x;
     const int r = tid & (ROWS - 1);
     const int cl = tid >> 4;                 // column within the workgroup
-    const int j0 = blockIdx.x * CPB;
+    // Workgroups go round-robin over the 8 XCDs, each with its own L2.  The ncb
+    // column blocks of one (batch, head) pair read the same key-side vectors, so
+    // they are numbered to run on one XCD: each run of 8 ncb consecutive
+    // workgroups holds 8 pairs, pair (8 g + x) on XCD x.
+    const int64_t grp = blockIdx.x / (XCDS * ncb);
+    const int within = (int)(blockIdx.x % (XCDS * ncb));
+    const int64_t bh = grp * XCDS + within % XCDS;
+    if (bh >= nbh) return;  // tail of the last run: the whole workgroup, before any barrier
+    const int j0 = (within / XCDS) * CPB;
     const int j = j0 + cl;
     const bool act = j < V;
     const int jc = act ? j : V - 1;
-    const int64_t bh = (int64_t)blockIdx.z * H + blockIdx.y;
     const TT* qb = q + bh * T * K;
     const TT* kb = k + bh * T * K;
     const TT* gb = g + bh * T * K;
@@ -188,8 +198,10 @@ ssm_status check_gdn2(const ssm_gdn2_dims* d) {
     if (d->batch < 1 || d->heads < 1 || d->seqlen < 0 || d->k_dim < 1 || d->v_dim < 1) return SSM_E_SHAPE;
     if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_E_DTYPE;
     if (d->k_dim != 16 && d->k_dim != 32 && d->k_dim != 64 && d->k_dim != 128) return SSM_E_UNSUPPORTED;
+    // one-dimensional grid of at most 2^31 workgroups
+    const int64_t ncb = (d->v_dim + 15) / 16, nbh = d->batch * d->heads;
     if (d->batch > 65535 || d->heads > 65535 || d->seqlen > ((int64_t)1 << 30) ||
-        d->v_dim > ((int64_t)1 << 30))
+        d->v_dim > ((int64_t)1 << 30) || (nbh + 7) / 8 * 8 * ncb >= ((int64_t)1 << 31))
         return SSM_E_UNSUPPORTED;
     return SSM_OK;
 }
@@ -198,9 +210,11 @@ template <typename TT, int R>
 ssm_status run(const ssm_gdn2_dims* d, const void* q, const void* k, const void* v, const void* g,
                const void* b, const void* w, const float* S0, float scale, void* o, float* S_last,
                ssm::Launcher& launch) {
-    const dim3 grid((unsigned)((d->v_dim + CPB - 1) / CPB), (unsigned)d->heads, (unsigned)d->batch);
-    return launch(SSM_K_GDN2_FWD, k_gdn2_fwd<TT, R>, grid, dim3(WG), (const TT*)q, (const TT*)k, (const TT*)v,
-                  (const TT*)g, (const TT*)b, (const TT*)w, S0, scale, (TT*)o, S_last, (int)d->heads,
+    const int64_t nbh = d->batch * d->heads;
+    const int ncb = (int)((d->v_dim + CPB - 1) / CPB);
+    const int64_t nwg = (nbh + XCDS - 1) / XCDS * XCDS * ncb;
+    return launch(SSM_K_GDN2_FWD, k_gdn2_fwd<TT, R>, dim3((unsigned)nwg), dim3(WG), (const TT*)q, (const TT*)k,
+                  (const TT*)v, (const TT*)g, (const TT*)b, (const TT*)w, S0, scale, (TT*)o, S_last, nbh, ncb,
                   (int)d->seqlen, (int)d->v_dim);
 }
 
