@@ -529,7 +529,10 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
         // Activations of the next (earlier) token are fetched before this token's
         // stores are issued: loads and stores retire in order, so a load issued
-        // after a store would also wait for that store.
+        // after a store would also wait for that store.  dy and z are read once and
+        // dx, ddt, dz written once: non-temporal, so that this streaming traffic
+        // does not push the block's checkpoint (read again at its first token)
+        // out of L2.
 #pragma unroll
         for (int i = TS - 1; i >= 0; --i) {
             if (i < cnt) {
@@ -541,8 +544,8 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 if (i > 0) {
                     const int64_t rp = (row - 1) * D + dc;
                     xn = x[rp];
-                    gn = dy[rp];
-                    if (GATE) zn = z[rp];
+                    gn = __builtin_nontemporal_load(&dy[rp]);
+                    if (GATE) zn = __builtin_nontemporal_load(&z[rp]);
                 }
                 if (GATE) {
                     sz = sigmoid_f(zv);
@@ -599,12 +602,12 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 const float ddelta = __builtin_fmaf(xv, s1, s2);
                 const float ddtv = ddelta * sgu;
                 if (act) {
-                    dxo[row * D + d] = from_f<T>(dxv_out);
-                    ddto[row * D + d] = from_f<T>(ddtv);
+                    __builtin_nontemporal_store(from_f<T>(dxv_out), &dxo[row * D + d]);
+                    __builtin_nontemporal_store(from_f<T>(ddtv), &ddto[row * D + d]);
                     if (GATE) {
                         const float ypre = __builtin_fmaf(Dd, xv, yacc);
                         const float dzv = dyv * ypre * sz * (1.0f + zv * (1.0f - sz));
-                        dzo[row * D + d] = from_f<T>(dzv);
+                        __builtin_nontemporal_store(from_f<T>(dzv), &dzo[row * D + d]);
                     }
                     dDacc = __builtin_fmaf(g, xv, dDacc);
                     ddtbacc += ddtv;
