@@ -231,34 +231,45 @@ __global__ __launch_bounds__(WG) void k_fwd_chunk(
 }
 
 // (2) chunk start states: starts(b, k) for k = 0..K-1, sequential over chunks.
+//     One lane per (batch, channel, state): the 16 states of a channel are
+//     independent here.  The chunk end states and delta sums are fetched CB
+//     chunks at a time, so that many loads are in flight per step of the
+//     sequential combine.
+constexpr int CB = 8;
+__device__ __forceinline__ float a2_of(const float* __restrict__ A_log, int64_t i) {
+    return -__builtin_amdgcn_exp2f(A_log[i] * LOG2E) * LOG2E;  // as load_A2
+}
 __global__ __launch_bounds__(WG) void k_fwd_carry(
     const float* __restrict__ A_log, const float* __restrict__ h0, const float* __restrict__ wsS,
     const float* __restrict__ wsSum, float* __restrict__ starts, int D, int K,
     int64_t start_nent, int64_t start_kstep) {
-    const int d = blockIdx.x * WG + threadIdx.x;
+    const int64_t DN = (int64_t)D * NS;
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;  // channel * NS + state
     const int b = blockIdx.z;
-    if (d >= D) return;
-    float A2[NS];
-    load_A2(A_log, d, A2);
-    float h[NS];
-    if (h0) load_state(h0 + ((int64_t)b * D + d) * NS, h);
-    else {
+    if (i >= DN) return;
+    const int64_t d = i / NS;
+    const float A2 = a2_of(A_log, i);
+    float h = h0 ? h0[(int64_t)b * DN + i] : 0.0f;
+    const int64_t e0 = (int64_t)b * (K - 1);  // entry of chunk 0 in wsS / wsSum
+    for (int k0 = 0; k0 < K - 1; k0 += CB) {
+        float Sb[CB], sb[CB];
 #pragma unroll
-        for (int n = 0; n < NS; ++n) h[n] = 0.0f;
-    }
-    for (int k = 0; k < K; ++k) {
-        store_state(starts + (((int64_t)b * start_nent + (int64_t)k * start_kstep) * D + d) * NS, h);
-        if (k == K - 1) break;
-        const int64_t e = ((int64_t)b * (K - 1) + k) * D + d;
-        float S[NS];
-        load_state(wsS + e * NS, S);
-        const float sumd = wsSum[e];
+        for (int j = 0; j < CB; ++j) {
+            if (k0 + j < K - 1) {
+                Sb[j] = wsS[(e0 + k0 + j) * DN + i];
+                sb[j] = wsSum[(e0 + k0 + j) * D + d];
+            }
+        }
 #pragma unroll
-        for (int n = 0; n < NS; ++n) {
-            const float P = __builtin_amdgcn_exp2f(A2[n] * sumd);
-            h[n] = __builtin_fmaf(P, h[n], S[n]);
+        for (int j = 0; j < CB; ++j) {
+            if (k0 + j < K - 1) {
+                starts[((int64_t)b * start_nent + (int64_t)(k0 + j) * start_kstep) * DN + i] = h;
+                const float P = __builtin_amdgcn_exp2f(A2 * sb[j]);
+                h = __builtin_fmaf(P, h, Sb[j]);
+            }
         }
     }
+    starts[((int64_t)b * start_nent + (int64_t)(K - 1) * start_kstep) * DN + i] = h;
 }
 
 // (3) recurrence of chunk k from its start; writes y, checkpoints and h_last.
@@ -410,31 +421,39 @@ __global__ __launch_bounds__(WG) void k_bwd_chunk(
 }
 
 // (2) adjoint entering each chunk from the right: Xin(b, k) = dL/dh at the
-//     chunk's last token from all later tokens; walks chunks in reverse.
+//     chunk's last token from all later tokens; walks chunks in reverse.  One
+//     lane per (batch, channel, state); the chunk adjoints and delta sums are
+//     fetched CB chunks at a time.
 __global__ __launch_bounds__(WG) void k_bwd_carry(
     const float* __restrict__ A_log, const float* __restrict__ wsG,
     const float* __restrict__ wsSum, float* __restrict__ Xin, int D, int K) {
-    const int d = blockIdx.x * WG + threadIdx.x;
+    const int64_t DN = (int64_t)D * NS;
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;  // channel * NS + state
     const int b = blockIdx.z;
-    if (d >= D) return;
-    float A2[NS];
-    load_A2(A_log, d, A2);
-    float X[NS];
+    if (i >= DN) return;
+    const int64_t d = i / NS;
+    const float A2 = a2_of(A_log, i);
+    float X = 0.0f;
+    const int64_t e0 = (int64_t)b * (K - 1) - 1;  // entry of chunk k is e0 + k (k >= 1)
+    for (int k0 = K - 1; k0 > 0; k0 -= CB) {
+        float Gb[CB], sb[CB];
 #pragma unroll
-    for (int n = 0; n < NS; ++n) X[n] = 0.0f;
-    for (int k = K - 1; k >= 0; --k) {
-        store_state(Xin + (((int64_t)b * K + k) * D + d) * NS, X);
-        if (k == 0) break;
-        const int64_t e = ((int64_t)b * (K - 1) + (k - 1)) * D + d;
-        float G[NS];
-        load_state(wsG + e * NS, G);
-        const float sumd = wsSum[e];
+        for (int j = 0; j < CB; ++j) {
+            if (k0 - j > 0) {
+                Gb[j] = wsG[(e0 + k0 - j) * DN + i];
+                sb[j] = wsSum[(e0 + k0 - j) * D + d];
+            }
+        }
 #pragma unroll
-        for (int n = 0; n < NS; ++n) {
-            const float P = __builtin_amdgcn_exp2f(A2[n] * sumd);
-            X[n] = __builtin_fmaf(P, X[n], G[n]);
+        for (int j = 0; j < CB; ++j) {
+            if (k0 - j > 0) {
+                Xin[((int64_t)b * K + k0 - j) * DN + i] = X;
+                const float P = __builtin_amdgcn_exp2f(A2 * sb[j]);
+                X = __builtin_fmaf(P, X, Gb[j]);
+            }
         }
     }
+    Xin[(int64_t)b * K * DN + i] = X;
 }
 
 // (3) per chunk: adjoint sweep in reverse over blocks of TS tokens.  Each block
@@ -644,7 +663,15 @@ __global__ __launch_bounds__(WG) void k_bwd_reduce_bc(const float* __restrict__ 
     const int v = (int)(i & 31);
     const float* p = wsBC + row * ndb * 32 + v;
     float s = 0.0f;
-    for (int blk = 0; blk < ndb; ++blk) s += p[blk * 32];
+    for (int b0 = 0; b0 < ndb; b0 += CB) {  // CB loads in flight, then the adds in order
+        float q[CB];
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+            if (b0 + j < ndb) q[j] = p[(b0 + j) * 32];
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+            if (b0 + j < ndb) s += q[j];
+    }
     if (v < NS) dB[row * NS + v] = from_f<T>(s);
     else dC[row * NS + (v - NS)] = from_f<T>(s);
 }
@@ -654,22 +681,36 @@ __global__ __launch_bounds__(WG) void k_bwd_reduce_params(
     const float* __restrict__ A_log, const float* __restrict__ wsPA,
     const float* __restrict__ wsPD, float* __restrict__ dA_log, float* __restrict__ dDo,
     float* __restrict__ ddt_bias, int Bt, int K, int D) {
-    const int i = blockIdx.x * WG + threadIdx.x;
-    if (i < D * NS) {
-        const int d = i / NS, n = i % NS;
+    const int64_t DN = (int64_t)D * NS;
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    const int64_t J = (int64_t)Bt * K;  // partials, summed in (batch, chunk) order
+    if (i < DN) {
         float s = 0.0f;
-        for (int b = 0; b < Bt; ++b)
-            for (int k = 0; k < K; ++k) s += wsPA[(((int64_t)b * K + k) * D + d) * NS + n];
+        for (int64_t j0 = 0; j0 < J; j0 += CB) {  // CB loads in flight, then the adds in order
+            float v[CB];
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                if (j0 + j < J) v[j] = wsPA[(j0 + j) * DN + i];
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                if (j0 + j < J) s += v[j];
+        }
         dA_log[i] = s * -expf(A_log[i]);
-    } else if (i < D * NS + D) {
-        const int d = i - D * NS;
+    } else if (i < DN + D) {
+        const int64_t d = i - DN;
         float s0 = 0.0f, s1 = 0.0f;
-        for (int b = 0; b < Bt; ++b)
-            for (int k = 0; k < K; ++k) {
-                const int64_t e = ((int64_t)b * K + k) * D + d;
-                s0 += wsPD[e * 2 + 0];
-                s1 += wsPD[e * 2 + 1];
-            }
+        for (int64_t j0 = 0; j0 < J; j0 += CB) {
+            float2 v[CB];
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                if (j0 + j < J) v[j] = reinterpret_cast<const float2*>(wsPD)[(j0 + j) * D + d];
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                if (j0 + j < J) {
+                    s0 += v[j].x;
+                    s1 += v[j].y;
+                }
+        }
         if (dDo) dDo[d] = s0;
         ddt_bias[d] = s1;
     }
@@ -881,7 +922,7 @@ ssm_status run_fwd(const Plan& p, const void* x, const void* dt, const void* B, 
     if (p.Kf > 1) {
         SSM_TRY(launch(SSM_K_FWD_CHUNK, k_fwd_chunk<T>, dim3(p.ndb, p.Kf - 1, p.Bt),
                        (const T*)x, (const T*)dt, (const T*)B, A_log, dt_bias, S, sum, L, D, Tc, K));
-        SSM_TRY(launch(SSM_K_FWD_CARRY, k_fwd_carry, dim3(p.ndb, 1, p.Bt), A_log, h0,
+        SSM_TRY(launch(SSM_K_FWD_CARRY, k_fwd_carry, dim3((unsigned)((p.D * NS + WG - 1) / WG), 1, p.Bt), A_log, h0,
                        (const float*)S, (const float*)sum, starts, D, K, nent, kstep));
     }
     return launch(SSM_K_FWD_MAIN, k_fwd_main<T, GATE>, dim3(p.ndb, p.Kf, p.Bt), (const T*)x,
@@ -909,7 +950,7 @@ ssm_status run_bwd(const Plan& p, const void* x, const void* dt, const void* B, 
         SSM_TRY(launch(SSM_K_BWD_CHUNK, k_bwd_chunk<T, GATE>, dim3(p.ndb, p.Kb - 1, p.Bt),
                        (const T*)dt, (const T*)C, (const T*)z, (const T*)dy, A_log, dt_bias, G,
                        sum, L, D, Tc, K));
-        SSM_TRY(launch(SSM_K_BWD_CARRY, k_bwd_carry, dim3(p.ndb, 1, p.Bt), A_log,
+        SSM_TRY(launch(SSM_K_BWD_CARRY, k_bwd_carry, dim3((unsigned)((p.D * NS + WG - 1) / WG), 1, p.Bt), A_log,
                        (const float*)G, (const float*)sum, X, D, K));
     }
     SSM_TRY(launch(SSM_K_BWD_MAIN, k_bwd_main<T, GATE>, dim3(p.ndb, p.Kb, p.Bt), (const T*)x,
