@@ -1,0 +1,80 @@
+"""The scan's results do not depend on what caller-owned buffers held before a call.
+
+Every byte of the checkpoint buffer, both workspaces and every output is first
+filled with 0xFF (a NaN in f32 and in bf16) and, in a second run, with zeros; the
+forward and the backward are then called through the C ABI.  Any value read
+before the library wrote it would show up as a NaN or as a difference between
+the two runs, so both runs must give finite outputs that are bitwise equal.
+Shapes: one chunk, several chunks in both directions with ragged ends, several
+channel blocks with a partial last block, f32 and bf16 activations.
+"""
+import ctypes
+
+import pytest
+import torch
+
+import workloads as W
+
+ssm = pytest.importorskip("selective_state_space_04_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _filled(nbytes, byte):
+    return torch.full((max(int(nbytes), 16),), byte, dtype=torch.uint8, device=DEV)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _run(t, io, byte):
+    lib = ssm.library()
+    bsz, L, din = t["x"].shape
+    dm = ssm.dims(bsz, L, din, 16, io)
+    ckpt = _filled(lib.ssm_scan_ckpt_bytes(ctypes.byref(dm)), byte)
+    nf, nb = lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(dm)), lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(dm))
+    wsf, wsb = _filled(nf, byte), _filled(nb, byte)
+    esz = 2 if io == torch.bfloat16 else 4
+    act = lambda shp: _filled(esz * shp[0] * shp[1] * shp[2], byte)[: esz * shp[0] * shp[1] * shp[2]]
+    f32 = lambda n: _filled(4 * n, byte)[: 4 * n]
+    y, dx, ddt, dz = (act((bsz, L, din)) for _ in range(4))
+    dB, dC = act((bsz, L, 16)), act((bsz, L, 16))
+    h_last, dh0 = f32(bsz * din * 16), f32(bsz * din * 16)
+    dA_log, dD, ddt_bias = f32(din * 16), f32(din), f32(din)
+    s = ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream)
+    rc = lib.ssm_scan_fwd(ctypes.byref(dm), _p(t["x"]), _p(t["dt"]), _p(t["B"]), _p(t["C"]), _p(t["z"]),
+                          _p(t["A_log"]), _p(t["D"]), _p(t["dt_bias"]), None, _p(y), _p(h_last), _p(ckpt),
+                          _p(wsf), nf, s, None)
+    assert rc == 0, ssm.status_str(rc)
+    rc = lib.ssm_scan_bwd(ctypes.byref(dm), _p(t["x"]), _p(t["dt"]), _p(t["B"]), _p(t["C"]), _p(t["z"]),
+                          _p(t["A_log"]), _p(t["D"]), _p(t["dt_bias"]), None, _p(ckpt), _p(t["dy"]), _p(dx),
+                          _p(ddt), _p(dB), _p(dC), _p(dz), _p(dA_log), _p(dD), _p(ddt_bias), _p(dh0), _p(wsb),
+                          nb, s, None)
+    assert rc == 0, ssm.status_str(rc)
+    torch.cuda.synchronize()
+    view = lambda b, dt: b.view(dt)
+    out = {"y": view(y, io), "dx": view(dx, io), "ddt": view(ddt, io), "dz": view(dz, io), "dB": view(dB, io),
+           "dC": view(dC, io), "h_last": view(h_last, torch.float32), "dh0": view(dh0, torch.float32),
+           "dA_log": view(dA_log, torch.float32), "dD": view(dD, torch.float32),
+           "ddt_bias": view(ddt_bias, torch.float32)}
+    return out
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape,bias", [((1, 64, 32), W.DT_BIAS_ACTIVE),      # one chunk
+                                        ((2, 1000, 100), W.DT_BIAS_SLOW),    # chunks with ragged ends
+                                        ((3, 777, 300), W.DT_BIAS_ACTIVE)])  # 2 channel blocks, partial
+def test_outputs_do_not_depend_on_prior_buffer_contents(shape, bias, io):
+    inp = W.make_inputs(*shape, seed=21, dt_bias=bias, bf16=io == torch.bfloat16)
+    t = {k: (None if v is None else torch.from_numpy(v).to(DEV)) for k, v in inp.items()}
+    for k in ("x", "z", "dt", "B", "C", "dy"):
+        t[k] = t[k].to(io).contiguous()
+    nan_run = _run(t, io, 0xFF)
+    zero_run = _run(t, io, 0x00)
+    for k in nan_run:
+        a, b = nan_run[k], zero_run[k]
+        assert torch.isfinite(a.float()).all(), f"{k}: non-finite values (a prior buffer value was read)"
+        assert torch.equal(a, b), f"{k}: differs between 0xFF- and zero-filled buffers"
