@@ -54,9 +54,10 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr int64_t TARGET_LANES = 262144;  // 4096 waves = 4 per SIMD
 constexpr int64_t MIN_CHUNK = 64;
 constexpr int64_t NUM_CU = 256;
-// Resident workgroups of the forward main kernel (7 waves/SIMD at its register
-// count) and of the backward main kernel (2 waves/SIMD), chip-wide.
-constexpr int64_t FWD_SLOTS = NUM_CU * 7;
+// Resident workgroups of the forward main kernel (6 waves/SIMD: 73-76 VGPRs in
+// its gated variants, allocated in steps of 8 out of 512) and of the backward
+// main kernel (2 waves/SIMD at 256 VGPRs), chip-wide.
+constexpr int64_t FWD_SLOTS = NUM_CU * 6;
 constexpr int64_t BWD_SLOTS = NUM_CU * 2;
 
 // ------------------------------------------------------------------ io helpers
