@@ -319,11 +319,9 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
     float Bn[NS], Cn[NS];
     load16(bp, Bn);
     load16(cp, Cn);
+    T ypend = T(0);  // output of the previous token, stored one token late
 #pragma unroll PF
     for (int i = 0; i < nt; ++i) {
-        // checkpoint: state before token t0+i (chunk starts k>0 come from the carry kernel)
-        if ((i & (TS - 1)) == 0 && ck && act && (i > 0 || k == 0))
-            store_state(ck + (int64_t)(i / TS) * ckstride, h);
         const float xv = to_f(xq[0]), dtv = to_f(dq[0]), zv = GATE ? to_f(zq[0]) : 0.0f;
 #pragma unroll
         for (int q = 0; q + 1 < PF; ++q) {
@@ -334,6 +332,13 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
         xq[PF - 1] = xs.raw(min(i + PF, nt - 1));
         dq[PF - 1] = ds.raw(min(i + PF, nt - 1));
         if (GATE) zq[PF - 1] = zs.raw(min(i + PF, nt - 1));
+        // the previous token's output and, every TS tokens, the checkpoint (state
+        // before token t0+i; chunk starts k>0 come from the carry kernel) are
+        // stored after this token's prefetch loads are issued: a later wait on a
+        // load would also wait for every store issued before it
+        if (i > 0 && act) yp[(int64_t)(i - 1) * D] = ypend;
+        if ((i & (TS - 1)) == 0 && ck && act && (i > 0 || k == 0))
+            store_state(ck + (int64_t)(i / TS) * ckstride, h);
         const int ip = min(i + 1, nt - 1);
         float Bv[NS], Cv[NS];
 #pragma unroll
@@ -346,9 +351,9 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
         float sg;
         const float delta = softplus_sig(dtv + bias, sg);
         const float acc = scan_token(h, A2, Bv, Cv, delta, xv);
-        const float yv = finish_y<GATE>(acc, Dd, xv, zv);
-        if (act) yp[(int64_t)i * D] = from_f<T>(yv);
+        ypend = from_f<T>(finish_y<GATE>(acc, Dd, xv, zv));
     }
+    if (nt > 0 && act) yp[(int64_t)(nt - 1) * D] = ypend;
     if (h_last && act && k == K - 1) store_state(h_last + ((int64_t)b * D + d) * NS, h);
 }
 
