@@ -484,6 +484,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     float* __restrict__ wsPA, float* __restrict__ wsPD, int L, int D, int Tc, int K,
     int64_t nck, int ndb) {
     constexpr int RS = 36;  // LDS row stride in floats: 16-byte aligned rows
+    static_assert(TS * 32 <= WG, "one dB/dC partial per thread at the block end");
     __shared__ float rows[NWAVE][64 * RS];
     __shared__ float wres[TS][2 * NWAVE][32];
     __shared__ float2 dsg[NWAVE][TS][64];  // per token: delta, sigmoid(dt + dt_bias)
@@ -511,6 +512,23 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const float* colp = rows[wave] + (half * 32) * RS + col;
     const int t0 = k * Tc, t1 = min(t0 + Tc, L);
     const int j0 = t0 / TS, j1 = (t1 + TS - 1) / TS;
+    // The outputs of a block's last-swept token (its first) and its dB/dC partial
+    // are stored after the next block's first loads have been issued: the memory
+    // counter is in order, so waiting for those loads would otherwise also wait
+    // for these stores.
+    T pdx = T(0), pddt = T(0), pdz = T(0);
+    int64_t prow = -1, pbc_at = -1;
+    float pbc = 0.0f;
+    auto flush = [&]() {
+        if (prow >= 0 && act) {
+            __builtin_nontemporal_store(pdx, &dxo[prow * D + d]);
+            __builtin_nontemporal_store(pddt, &ddto[prow * D + d]);
+            if (GATE) __builtin_nontemporal_store(pdz, &dzo[prow * D + d]);
+        }
+        if (pbc_at >= 0) wsBC[pbc_at] = pbc;
+        prow = -1;
+        pbc_at = -1;
+    };
     for (int j = j1 - 1; j >= j0; --j) {
         const int ts = j * TS;
         const int cnt = min(TS, t1 - ts);
@@ -529,6 +547,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             float hs[NS];
             load_state(ckp, hs);
             T xr = x[row0 * D + dc], dr = dt[row0 * D + dc];
+            flush();  // the previous block's deferred stores
 #pragma unroll
             for (int i = 0; i < TS; ++i) {
                 if (i < cnt) {
@@ -626,29 +645,39 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 const float dxv_out = __builtin_fmaf(delta, s1, Dd * g);
                 const float ddelta = __builtin_fmaf(xv, s1, s2);
                 const float ddtv = ddelta * sgu;
-                if (act) {
+                float dzv = 0.0f;
+                if (GATE) {
+                    const float ypre = __builtin_fmaf(Dd, xv, yacc);
+                    dzv = dyv * ypre * sz * (1.0f + zv * (1.0f - sz));
+                }
+                if (i == 0) {  // stored after the next block's first loads
+                    pdx = from_f<T>(dxv_out);
+                    pddt = from_f<T>(ddtv);
+                    pdz = from_f<T>(dzv);
+                    prow = row;
+                } else if (act) {
                     __builtin_nontemporal_store(from_f<T>(dxv_out), &dxo[row * D + d]);
                     __builtin_nontemporal_store(from_f<T>(ddtv), &ddto[row * D + d]);
-                    if (GATE) {
-                        const float ypre = __builtin_fmaf(Dd, xv, yacc);
-                        const float dzv = dyv * ypre * sz * (1.0f + zv * (1.0f - sz));
-                        __builtin_nontemporal_store(from_f<T>(dzv), &dzo[row * D + d]);
-                    }
+                    if (GATE) __builtin_nontemporal_store(from_f<T>(dzv), &dzo[row * D + d]);
+                }
+                if (act) {
                     dDacc = __builtin_fmaf(g, xv, dDacc);
                     ddtbacc += ddtv;
                 }
             }
         }
         __syncthreads();
-        for (int idx = threadIdx.x; idx < cnt * 32; idx += WG) {
-            const int i = idx >> 5, v = idx & 31;
+        if (threadIdx.x < cnt * 32) {  // one (token, value) per thread: cnt * 32 <= WG
+            const int i = threadIdx.x >> 5, v = threadIdx.x & 31;
             float s = wres[i][0][v];
 #pragma unroll
             for (int w = 1; w < 2 * NWAVE; ++w) s += wres[i][w][v];
-            wsBC[((row0 + i) * ndb + blockIdx.x) * 32 + v] = s;
+            pbc = s;  // stored after the next block's first loads
+            pbc_at = ((row0 + i) * ndb + blockIdx.x) * 32 + v;
         }
         __syncthreads();
     }
+    flush();
     if (act) {
         const int64_t e = ((int64_t)b * K + k) * D + d;
         store_state(wsPA + e * NS, dA);
