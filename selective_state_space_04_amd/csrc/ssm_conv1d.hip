@@ -15,7 +15,7 @@
 //     token), so a wave reads 64 * VEC channels of one token as one coalesced
 //     512 B / 1 KB row; rows whose d_inner is not a multiple of 4 use VEC = 1.
 //   * A wave streams a run of TT = 64 tokens with a sliding window of the last
-//     K inputs in registers, PF = 8 tokens of loads in flight; the 4 waves of a
+//     K inputs in registers, PF = 4 tokens of loads in flight; the 4 waves of a
 //     workgroup take 4 consecutive runs, so the K-1 token halo a run re-reads
 //     was just read by its neighbour (L2 hit).
 //   * Backward: g = dy * silu'(pre) needs the forward's pre, recomputed from the
@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "ssm_common.h"
 #include "ssm_conv1d.h"
@@ -76,11 +78,14 @@ template <typename T, int VEC> __device__ __forceinline__ void st(T* p, const fl
 template <> __device__ __forceinline__ void st<float, 4>(float* p, const float v[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
+// two floats to two bf16 (round to nearest even) in one packed conversion
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 template <> __device__ __forceinline__ void st<bf16_t, 4>(bf16_t* p, const float v[4]) {
-    uint2 u;
-    u.x = (uint32_t)from_f<bf16_t>(v[0]) | ((uint32_t)from_f<bf16_t>(v[1]) << 16);
-    u.y = (uint32_t)from_f<bf16_t>(v[2]) | ((uint32_t)from_f<bf16_t>(v[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = u;
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 template <> __device__ __forceinline__ void st<float, 1>(float* p, const float v[1]) { p[0] = v[0]; }
 template <> __device__ __forceinline__ void st<bf16_t, 1>(bf16_t* p, const float v[1]) {
@@ -180,15 +185,21 @@ __global__ __launch_bounds__(WG) void k_conv_fwd(const T* __restrict__ x, const 
         R q[PF];
 #pragma unroll
         for (int p = 0; p < PF; ++p) q[p] = ld<T, VEC>(xp + (int64_t)(t0 + p) * D);
-        for (int u = t0; u < t1; u += PF) {
+        // Every group of PF tokens but the last fetches the PF tokens after it, all
+        // inside the run: with no per-token fetch test the queue is refilled in
+        // place, so no wait on the loads just issued is needed at the loop's end.
+        auto group = [&](int u, auto fetch) {
 #pragma unroll
             for (int p = 0; p < PF; ++p) {
                 unpack(q[p], win[K - 1]);
-                if (u + p + PF < t1) q[p] = ld<T, VEC>(xp + (int64_t)(u + p + PF) * D);
+                if constexpr (decltype(fetch)::value) q[p] = ld<T, VEC>(xp + (int64_t)(u + p + PF) * D);
                 fwd_token<T, K, VEC>(wk, bs, win, yp + (int64_t)(u + p) * D);
                 shift_window<K, VEC>(win);
             }
-        }
+        };
+        int u = t0;
+        for (; u + PF < t1; u += PF) group(u, std::true_type{});
+        group(u, std::false_type{});
     } else {
         for (int u = t0; u < t1; ++u) {
             unpack(ld<T, VEC>(xp + (int64_t)u * D), win[K - 1]);
