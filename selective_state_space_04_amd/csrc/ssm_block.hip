@@ -19,8 +19,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <deque>
 #include <initializer_list>
-#include <vector>
 
 #include "ssm_block.h"
 #include "ssm_common.h"
@@ -39,7 +39,7 @@ struct LtPlan {
 
 struct ssm_block_ctx {
     hipblasLtHandle_t lt;
-    std::vector<LtPlan> plans;
+    std::deque<LtPlan> plans;  // a deque: adding a plan keeps earlier plans where they are
 };
 
 namespace {
