@@ -1,22 +1,27 @@
-"""Throughput of the S6 selective scan (forward + backward) on one MI355X.
+"""Throughput of the S6 selective scan on one MI355X.
 
-One step = ssm_scan_fwd (training, writes checkpoints) + ssm_scan_bwd over one
-batch of the Mamba-2.8B-shaped workload: batch 4, seqlen 8192, d_inner 5120,
-d_state 16, bf16 activations, f32 state and arithmetic.  Inputs are seeded
-synthetic tensors already resident in HBM.  The metric is elements
-(batch*seqlen*d_inner*d_state) per second.
+One step of the default workload = ssm_scan_fwd (training, writes checkpoints)
++ ssm_scan_bwd over one batch of the Mamba-2.8B-shaped workload: batch 4,
+seqlen 8192, d_inner 5120, d_state 16, bf16 activations, f32 state and
+arithmetic.  --config picks another of the five scan workloads (the tiny f32
+case, the Mamba-130M-shaped forward and forward+backward, the decode chain).
+Inputs are seeded synthetic tensors already resident in HBM.  The metric is
+elements (batch*seqlen*d_inner*d_state) per second; each timed step starts
+after 512 MiB of unrelated writes (the flushed time is `value`, the
+back-to-back time is reported beside it).
 
 Prints ONE JSON line.  Besides the contract fields it carries
-  roofline      : the dominant kernel against the bound that limits it, the f32
-                  vector ALU: its algorithmic flops per launch / its average
-                  launch time (HIP events recorded by the library around each
-                  launch on the launch stream), against 157.3 TFLOP/s;
-  roofline_hbm  : the same kernel's algorithmic bytes per launch / launch time,
-                  against 8 TB/s HBM;
+  roofline      : the dominant kernel against HBM bandwidth: its algorithmic
+                  bytes per launch (inputs read once, outputs written once) /
+                  its average launch time (HIP events the library records
+                  around each launch on the launch stream), against 8 TB/s,
+                  and against a plain device copy measured in the same run;
+                  `traffic` is its profiler-counted bytes when they were taken
+                  on the current kernel source, else null;
+  valu          : the same kernel's counted VALU lane instructions per second
+                  against the non-packed issue peak (when counted on this source);
+  step_hbm      : the whole step's algorithmic bytes / step time;
   cpu_baseline  : the f64 oracle timed on a bounded sample on the host cores.
-The measured HBM traffic of the dominant kernel (profiler byte counters, scaled
-by a plain copy of known size) is taken from profiles/ when it was recorded for
-the current kernel source, else null.
 """
 import argparse
 import json
@@ -29,7 +34,6 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-F32_VECTOR_PEAK_TFLOPS = 157.3
 CSRC = os.path.join(ROOT, "selective_state_space_04_amd", "csrc")
 # (kernel source, committed counter summary) per workload
 TRAFFIC = {"scan": (os.path.join(CSRC, "ssm_scan.hip"),
@@ -41,27 +45,16 @@ TRAFFIC = {"scan": (os.path.join(CSRC, "ssm_scan.hip"),
            "gdn2": (os.path.join(CSRC, "ssm_gdn2.hip"),
                     os.path.join(ROOT, "profiles", "gdn2_b4h16t4096_traffic.txt"))}
 
-# Algorithmic f32 flops per element (b,t,d,n), FMA = 2, mul/add/exp = 1.
-#  forward main : exp(dt*A) (mul + exp), dt*x*B (mul), h update (FMA), C.h (FMA)  = 7
-#  backward main: state recompute (mul + exp + mul + FMA = 5); adjoint update
-#                 (FMA), lambda.B for dx/ddelta (FMA), dB product (mul), dC product
-#                 (mul), carry lambda*a (mul), times h_prev (mul), A-term of
-#                 ddelta (FMA), dA (FMA), C.h for the gate gradient (FMA) = 14;
-#                 the two sums over channels for dB and dC (2 adds)         = 21
-FLOPS_PER_ELEMENT = {"k_fwd_main": 7, "k_bwd_main": 21}
-
-
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c4_mamba2p8b_bf16")
+    ap.add_argument("--config", default="c4_mamba2p8b_bf16",
+                    choices=("c1_tiny", "c2_mamba130m_fwd", "c3_mamba130m_fwdbwd", "c4_mamba2p8b_bf16",
+                             "c5_decode_step"),
+                    help="scan workload (c5_decode_step runs the decode bench)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=4,
-                    help="batch rows the oracle baseline runs on (all tokens)")
-    ap.add_argument("--cpu-sample-channels", type=int, default=0,
-                    help="channels the oracle baseline runs on (0 = all)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--op", choices=("scan", "conv1d", "decode", "block", "block-c", "train", "gdn2"),
                     default="scan",
@@ -108,26 +101,6 @@ def measured_traffic(kernel, op="scan"):
         return None
     f = dict(p.split("=") for p in kv[kernel])
     return int(float(f["fetch_bytes"]) + float(f["write_bytes"]))
-
-
-def cpu_baseline(inp, cfg, rows, channels):
-    import numpy as np
-
-    import oracle
-    dsel = slice(0, channels)
-    sub = {k: np.ascontiguousarray(inp[k][:rows, :, dsel]) for k in ("x", "z", "dt", "dy")}
-    sub.update({k: np.ascontiguousarray(inp[k][:rows]) for k in ("B", "C")})
-    sub.update({"A_log": inp["A_log"][dsel], "D": inp["D"][dsel], "dt_bias": inp["dt_bias"][dsel]})
-    sub = {k: v.astype(np.float64) for k, v in sub.items()}
-    t0 = time.perf_counter()
-    oracle.fwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"], sub["A_log"], sub["D"], sub["dt_bias"])
-    oracle.bwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"], sub["A_log"], sub["D"], sub["dt_bias"],
-               sub["dy"])
-    sec = time.perf_counter() - t0
-    elems = rows * cfg["seqlen"] * channels * cfg["d_state"]
-    return {"value": elems / sec, "unit": "elements/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"batch rows 0..{rows - 1}, all {cfg['seqlen']} tokens, channels 0..{channels - 1} of "
-                      f"the same workload, fwd+bwd in f64 ({elems} elements, {sec:.1f} s)"}
 
 
 def copy_probe(dev):
@@ -280,6 +253,7 @@ def decode_bench(args):
             out.append(e0.elapsed_time(e1))
         return float(np.median(out))
 
+    copy_gbps = copy_bandwidth(dev)
     h.zero_()
     run()  # warm-up
     torch.cuda.synchronize()
@@ -330,7 +304,13 @@ def decode_bench(args):
         "graph": {"value": elems / (graph_ms * 1e-3), "replays_bitwise_equal_eager": replays},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": "k_step",
-                     "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes_per_launch": per_step},
+                     "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes_per_launch": per_step,
+                     "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(gbps / copy_gbps, 4),
+                     "cache_resident": "the 84 MB state (batch 256 x 5120 x 16 f32) fits the 256 MB "
+                                       "Infinity Cache and is not flushed between steps (decode keeps it "
+                                       "hot by design); byte counters count traffic past L2, which "
+                                       "includes Infinity Cache hits, so this rate is not proof of HBM "
+                                       "bandwidth"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -347,7 +327,8 @@ def decode_bench(args):
         line["cpu_baseline"] = {"value": rows * D * N * steps / sec, "unit": "elements/s",
                                 "cores": oracle.num_threads(), "kind": "oracle",
                                 "sample": f"batch rows 0..{rows - 1}, all {D} channels, the first {steps} steps "
-                                          f"of the same workload in f64 ({sec:.1f} s, host copies included)"}
+                                          f"of the same workload in f64 ({sec:.1f} s, host copies included)",
+                                **host_cpu()}
     out = json.dumps(line)
     print(out, flush=True)
     if args.out:
@@ -649,31 +630,121 @@ def block_c_bench(args):
             f.write(out + "\n")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the scan is measured on a "
-              f"single MI355X and multi-GPU sharding is design-only.", file=sys.stderr)
-        sys.exit(2)
-    if args.op == "conv1d":
-        conv_bench(args)
-        return
-    if args.op == "decode":
-        decode_bench(args)
-        return
-    if args.op == "block":
-        block_bench(args)
-        return
-    if args.op == "train":
-        train_bench(args)
-        return
-    if args.op == "block-c":
-        block_c_bench(args)
-        return
-    if args.op == "gdn2":
-        gdn2_bench(args)
-        return
+# Algorithmic bytes per launch of the kernels that carry a pass's compulsory
+# traffic (every input read once, every output written once); carries, chunk
+# passes and reductions only add overhead on top of these.
+def kernel_alg_bytes(kernel, cfg, esz):
+    ab = algorithmic_bytes(cfg, esz)
+    if kernel.startswith("k_fwd_main") or kernel.startswith("k_fwd_tile"):
+        return ab["fwd_main"]
+    if kernel.startswith("k_bwd_main") or kernel.startswith("k_bwd_tile"):
+        return ab["bwd_main"]
+    return None
 
+
+def host_cpu():
+    """The host's CPU model and the cores this process may use."""
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cores_available": avail}
+
+
+def copy_bandwidth(dev, nbytes=1 << 30, reps=5):
+    """Read+write GB/s of a plain device copy of nbytes (best of reps): the
+    attainable-bandwidth reference the HBM fraction is also reported against."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return 2 * nbytes / (best * 1e-3) / 1e9
+
+
+def counted_valu(kernel, op="scan"):
+    """(VALU lane instructions, transcendental lane instructions) per launch of
+    `kernel` from the committed SQ counter summary, or None when it was taken on
+    another kernel source."""
+    import hashlib
+    src_path, _ = TRAFFIC[op]
+    path = os.path.join(ROOT, "profiles", "c4_mamba2p8b_bf16_valu.txt")
+    try:
+        lines = open(path).read().split("\n")
+        src = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    kv = {}
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) >= 2 and not ln.startswith("#"):
+            kv[parts[0]] = parts[1:]
+    if kv.get("source_sha256", [None])[0] != src or kernel not in kv:
+        return None
+    f = dict(p.split("=") for p in kv[kernel])
+    return float(f["valu_wave_insts"]) * 64, float(f["trans_wave_insts"]) * 64
+
+
+# One SIMD issues one wave64 VALU instruction per 4 cycles (16 lanes wide), so
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 3.93e13 lane instructions per second
+# without packed FP32 (which this library does not use).
+VALU_LANE_PEAK = 256 * 4 * 16 * 2.4e9
+
+
+def cpu_scan_baseline(inp, cfg, passes, budget_s=12.0):
+    """The oracle on the host cores: the whole workload when it fits the time
+    budget (repeated when tiny), else the leading batch rows that fit."""
+    import numpy as np
+
+    import oracle
+    bsz, L, D = inp["x"].shape
+    N = cfg["d_state"]
+    bwd = "bwd" in passes
+
+    def run(rows):
+        sub = {k: inp[k][:rows] for k in ("x", "z", "dt", "B", "C") + (("dy",) if bwd else ())}
+        t0 = time.perf_counter()
+        oracle.fwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"], inp["A_log"], inp["D"], inp["dt_bias"])
+        if bwd:
+            oracle.bwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"], inp["A_log"], inp["D"], inp["dt_bias"],
+                       sub["dy"])
+        return time.perf_counter() - t0
+
+    sec1 = run(1)
+    per_row = max(sec1, 1e-6)
+    if per_row * bsz <= budget_s:
+        reps = max(1, int(budget_s / (per_row * bsz) / 4))
+        sec = sum(run(bsz) for _ in range(reps))
+        rows, what = bsz, f"the whole workload ({bsz} rows), {reps} run(s)"
+    else:
+        rows = max(1, min(bsz, int(budget_s / per_row)))
+        reps = 1
+        sec = run(rows)
+        what = f"batch rows 0..{rows - 1} of {bsz}, all {L} tokens and {D} channels"
+    elems = reps * rows * L * D * N
+    return {"value": elems / sec, "unit": "elements/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{what}, {'fwd+bwd' if bwd else 'fwd'} in f64 ({elems} elements, {sec:.1f} s)",
+            **host_cpu()}
+
+
+def scan_bench(args):
     import numpy as np
     import torch
 
@@ -681,15 +752,15 @@ def main():
     import workloads as W
 
     cfg = W.CONFIGS[args.config]
-    if "bwd" not in cfg["passes"]:
-        raise SystemExit(f"{args.config} is not a fwd+bwd workload")
+    passes = cfg["passes"]
+    bwd = "bwd" in passes
     dev = torch.device("cuda:0")
     io = torch.bfloat16 if cfg["io"] == "bf16" else torch.float32
     esz = 2 if io == torch.bfloat16 else 4
     print(f"[bench] generating {args.config} inputs", file=sys.stderr, flush=True)
     inp = W.make_config(args.config)
     t = {}
-    for k in ("x", "z", "dt", "B", "C", "dy"):
+    for k in ("x", "z", "dt", "B", "C") + (("dy",) if bwd else ()):
         t[k] = torch.from_numpy(inp[k]).to(dev).to(io)
     for k in ("A_log", "D", "dt_bias"):
         t[k] = torch.from_numpy(inp[k]).to(dev)
@@ -703,26 +774,41 @@ def main():
 
     def step(timer=None):
         _, _, ckpt = ssm.ssm_scan_fwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"],
-                                      t["dt_bias"], training=True, y=y, timing=timer)
-        ssm.ssm_scan_bwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"], ckpt,
-                         t["dy"], out=grads, timing=timer)
+                                      t["dt_bias"], training=bwd, y=y, timing=timer)
+        if bwd:
+            ssm.ssm_scan_bwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"], ckpt,
+                             t["dy"], out=grads, timing=timer)
 
     if args.copy_probe:
         copy_probe(dev)
+    copy_gbps = copy_bandwidth(dev)
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Flushed: 512 MiB (twice the 256 MB Infinity Cache) written between steps,
+    # outside each step's events, so that every step starts from cold caches.
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
     timers = [ssm.LaunchTimer() for _ in range(args.steps)]
-    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        ev[i][0].record()
+        step(timers[i])
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # Unflushed: the same steps back to back.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(timers[i])
-    e1.record(stream)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms_hot = e0.elapsed_time(e1) / args.steps
+    del flush
     per_kernel = {}
     for tm in timers:
         for name, kms in tm.results():
@@ -733,23 +819,29 @@ def main():
     kcount = {k: len(v) // args.steps for k, v in per_kernel.items()}
     dominant = max(kavg, key=lambda k: kavg[k] * kcount[k])
     ab = algorithmic_bytes(cfg, esz)
-    dom_bytes = {"k_bwd_main": ab["bwd_main"], "k_fwd_main": ab["fwd_main"]}.get(dominant)
+    step_bytes = ab["fwd"] + (ab["bwd"] if bwd else 0)
     elems = bsz * L * D * N
-    roof = roof_hbm = None
+    dom_bytes = kernel_alg_bytes(dominant, cfg, esz)
+    roof = valu = None
     if dom_bytes is not None:
         sec = kavg[dominant] * 1e-3
         traffic = measured_traffic(dominant)
-        flops = FLOPS_PER_ELEMENT[dominant] * elems
-        tflops = flops / sec / 1e12
-        roof = {"bound": "alu", "achieved": round(tflops, 2), "peak": F32_VECTOR_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / F32_VECTOR_PEAK_TFLOPS, 4), "traffic": traffic,
-                "kernel": dominant, "kernel_ms": round(kavg[dominant], 4),
-                "algorithmic_flops_per_launch": flops, "flops_per_element": FLOPS_PER_ELEMENT[dominant]}
         gbps = dom_bytes / sec / 1e9
-        roof_hbm = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dominant,
-                    "algorithmic_bytes_per_launch": dom_bytes,
-                    "measured_GBps": None if traffic is None else round(traffic / sec / 1e9, 1)}
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dominant,
+                "kernel_ms": round(kavg[dominant], 4), "algorithmic_bytes_per_launch": dom_bytes,
+                "traffic_over_algorithmic": None if traffic is None else round(traffic / dom_bytes, 3),
+                "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(gbps / copy_gbps, 4)}
+        cv = counted_valu(dominant) if args.config == "c4_mamba2p8b_bf16" else None
+        if cv is not None:
+            lane, trans = cv
+            valu = {"kernel": dominant, "lane_insts_per_element": round(lane / elems, 2),
+                    "trans_lane_insts_per_element": round(trans / elems, 2),
+                    "achieved_lane_insts_per_s": lane / sec, "peak_lane_insts_per_s": VALU_LANE_PEAK,
+                    "frac": round(lane / sec / VALU_LANE_PEAK, 4),
+                    "note": "SQ_INSTS_VALU x 64 from the committed counters; peak = one wave64 VALU "
+                            "instruction per SIMD per 4 cycles at 2.4 GHz, no packed FP32"}
+    work = "fwd+bwd" if bwd else "fwd (inference: no checkpoints)"
     line = {
         "metric": "selective-scan fwd+bwd elements(B\u00b7L\u00b7D\u00b7N)/s and achieved HBM GB/s",
         "value": elems / (ms * 1e-3),
@@ -764,23 +856,39 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.config}: batch={bsz} seqlen={L} d_inner={D} d_state={N}, "
-                               f"{cfg['io']} activations, f32 state, fwd+bwd",
-                   "batch": bsz, "seqlen": L, "d_inner": D, "d_state": N, "io_dtype": cfg["io"]},
-        "achieved_hbm_GBps": round((ab["fwd"] + ab["bwd"]) / (ms * 1e-3) / 1e9, 1),
+                               f"{cfg['io']} activations, f32 state, {work}",
+                   "batch": bsz, "seqlen": L, "d_inner": D, "d_state": N, "io_dtype": cfg["io"], "passes": work},
+        "timing": {"ms_per_step_flushed": round(ms, 4), "ms_per_step_unflushed": round(ms_hot, 4),
+                   "flush": "512 MiB written between timed steps, outside each step's events"},
+        "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "frac_of_copy": round(step_bytes / (ms * 1e-3) / 1e9 / copy_gbps, 4)},
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kavg.items())},
         "roofline": roof,
-        "roofline_hbm": roof_hbm,
+        "valu": valu,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        ch = args.cpu_sample_channels or D
-        line["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_rows, bsz), min(ch, D))
+        line["cpu_baseline"] = cpu_scan_baseline(inp, cfg, passes)
     s = json.dumps(line)
     print(s, flush=True)
     if args.out:
         with open(args.out, "w") as f:
             f.write(s + "\n")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the scan is measured on a "
+              f"single MI355X and multi-GPU sharding is design-only.", file=sys.stderr)
+        sys.exit(2)
+    if args.op == "scan" and args.config == "c5_decode_step":
+        args.op = "decode"
+    ops = {"conv1d": conv_bench, "decode": decode_bench, "block": block_bench, "train": train_bench,
+           "block-c": block_c_bench, "gdn2": gdn2_bench, "scan": scan_bench}
+    ops[args.op](args)
 
 
 if __name__ == "__main__":

@@ -4,10 +4,14 @@
  *
  * Source of the operation: the rustytorch commit log, page
  * "crates/training/rtx-transformers/tests":
- *   - the commit replacing the MambaBlock stub runs in_proj -> causal depthwise
- *     conv1d -> SiLU -> x_proj -> (dt, B, C) -> delta = softplus(dt . dt_proj +
- *     dt_bias) -> selective scan with the D skip -> gate by SiLU(z) -> out_proj,
- *     with the residual outside the block;
+ *   - the commit replacing the MambaBlock stub defines the block; written as
+ *     equations over tokens (rows) of X [T, d_model]:
+ *         [u | z]        = X W_in^T                  (two d_inner halves)
+ *         v              = silu(conv1d_causal(u; conv_w) + conv_b)
+ *         [r | B | C]    = v W_x^T                   (dt_rank, d_state, d_state)
+ *         delta          = softplus(r W_dt^T + dt_bias)
+ *         y              = scan(v, delta, B, C; A_log, D) * silu(z)
+ *         Y              = y W_out^T                 (residual added by the caller);
  *   - the hand-written VJP commit returns gradients for in_proj, conv1d_weight,
  *     conv1d_bias, A_log, x_proj, dt_proj, dt_bias, D and out_proj, summed over
  *     the batch;

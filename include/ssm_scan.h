@@ -115,7 +115,9 @@ enum {
     SSM_K_CONV_STEP = 14,    /* one token through the conv ring */
     SSM_K_CONV_RING = 15,    /* ring copies/fills when seqlen == 0 */
     SSM_K_BLOCK_BC = 16,     /* x_proj's B/C columns split / joined (ssm_block.h) */
-    SSM_K_GDN2_FWD = 17      /* Gated DeltaNet-2 forward recurrence (ssm_gdn2.h) */
+    SSM_K_GDN2_FWD = 17,     /* Gated DeltaNet-2 forward recurrence (ssm_gdn2.h) */
+    SSM_K_TILE_INIT = 18,    /* zeroes the tile tickets/flags, writes the A*log2(e) table */
+    SSM_K_FWD_TILE = 19      /* tiled forward: segments in registers, chained tile carries */
 };
 
 /* Name of a kernel id (for matching profiler output); "?" if unknown. */
@@ -154,6 +156,13 @@ ssm_status ssm_scan_fwd(const ssm_dims *dims, const void *x, const void *dt, con
 /* Backward: the reverse-time adjoint of ssm_scan_fwd for L = sum(dy * y)
  * (commit adding the hand-written VJP).  Needs the ckpt written by
  * ssm_scan_fwd with the same dims and inputs.
+ *   h0                      : NOT READ.  The initial state reaches the backward
+ *                             through ckpt, whose first entry ssm_scan_fwd wrote
+ *                             from the h0 it was given; the argument exists so
+ *                             that both calls take the same list, and may be
+ *                             NULL.  A different h0 here changes nothing: to
+ *                             differentiate at another initial state, rerun
+ *                             ssm_scan_fwd with it.
  *   dy                      : [Bt, L, D] upstream gradient, io dtype
  *   dx, ddt, dz             : [Bt, L, D] io dtype; ddt is w.r.t. the raw dt input
  *                             (d delta * sigmoid(dt + dt_bias)); dz required iff z

@@ -6,12 +6,12 @@ TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 library.
 
 Definition (rustytorch commit log, page "crates/training/rtx-transformers/
-tests": the commit replacing the MambaBlock stub lists the forward in_proj ->
-causal depthwise conv1d -> SiLU -> x_proj -> (dt, B, C) -> delta =
-softplus(dt . dt_proj + dt_bias) -> scan -> gate by SiLU(z) -> out_proj, with
-the residual outside the block; the hand-written VJP commit returns gradients
-for in_proj, conv1d_weight, conv1d_bias, A_log, x_proj, dt_proj, dt_bias, D and
-out_proj, summed over the batch).
+tests": the commit replacing the MambaBlock stub defines the block, here as
+equations over token rows of X: [u | z] = X W_in^T; v = silu(causal depthwise
+conv of u + conv_b); [r | B | C] = v W_x^T; delta = softplus(r W_dt^T + dt_bias);
+y = scan(v, delta, B, C) * silu(z); Y = y W_out^T, the residual being the
+caller's.  The hand-written VJP commit gives the parameter list whose gradients
+are returned, each summed over the batch).
 
 Readings where the pages are silent: the projections are bias-free linear maps
 y = x W^T with PyTorch's [out, in] weight layout; in_proj's first d_inner

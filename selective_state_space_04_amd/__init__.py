@@ -16,6 +16,7 @@ and, in front of it, the causal depthwise conv1d + SiLU with its conv ring
 (same page: the real-S6-forward commit's in_proj -> conv1d -> SiLU -> x_proj).
 """
 import ctypes
+import functools
 import os
 
 import torch
@@ -173,6 +174,27 @@ def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _on_stream(fn):
+    """Runs an entry point with its `stream` made current while it allocates.
+
+    Workspaces, checkpoints and fresh outputs come from torch's caching
+    allocator, which ties each block to the stream current at allocation.  A
+    workspace freed when the call returns goes back to that stream's pool, so it
+    must be allocated on the stream the kernels run on; otherwise the next
+    allocation on the current stream could reuse it while the launched kernels
+    still read it.  Outputs returned from a call with an explicit stream belong
+    to that stream (use Tensor.record_stream before reading them elsewhere)."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        s = kwargs.get("stream")
+        if s is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(s):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
+@_on_stream
 def ssm_scan_fwd(x, dt, B, C, z, A_log, D, dt_bias, h0=None, *, training=False,
                  return_last_state=False, y=None, stream=None, timing=None):
     """Forward scan.  x, dt, z: [batch, L, d_inner]; B, C: [batch, L, 16] (float32 or
@@ -208,10 +230,13 @@ def ssm_scan_fwd(x, dt, B, C, z, A_log, D, dt_bias, h0=None, *, training=False,
     return y, h_last, ckpt
 
 
+@_on_stream
 def ssm_scan_bwd(x, dt, B, C, z, A_log, D, dt_bias, ckpt, dy, h0=None, *, want_dh0=False,
                  stream=None, timing=None, out=None):
     """Backward of ssm_scan_fwd for the loss sum(dy * y).  Returns a dict with dx, ddt,
-    dz (None without z), dB, dC (io dtype) and dA_log, dD, ddt_bias, dh0 (float32)."""
+    dz (None without z), dB, dC (io dtype) and dA_log, dD, ddt_bias, dh0 (float32).
+    h0 is shape-checked but not read: the initial state comes from ckpt, which the
+    forward wrote from its own h0."""
     dev = x.device
     bsz, L, din = x.shape
     io = x.dtype
@@ -247,6 +272,7 @@ def ssm_scan_bwd(x, dt, B, C, z, A_log, D, dt_bias, ckpt, dy, h0=None, *, want_d
     return g
 
 
+@_on_stream
 def ssm_scan_step(h, x, dt, B, C, z, A_log, D, dt_bias, *, y=None, stream=None, timing=None):
     """One token: h [batch, d_inner, 16] float32 is updated in place; x, dt, z
     [batch, d_inner] and B, C [batch, 16] in the io dtype.  Returns y [batch, d_inner]."""
@@ -288,6 +314,7 @@ def _ring(t, name, bsz, din, k, dev, required=False):
     return t
 
 
+@_on_stream
 def ssm_conv1d_fwd(x, w, bias=None, ring0=None, *, return_ring=False, y=None, stream=None, timing=None):
     """Causal depthwise conv1d + SiLU.  x [batch, L, d_inner] (float32 or bfloat16);
     w [d_inner, d_conv] float32 (PyTorch's [d_inner, 1, d_conv] squeezed); bias
@@ -312,6 +339,7 @@ def ssm_conv1d_fwd(x, w, bias=None, ring0=None, *, return_ring=False, y=None, st
     return y, ring_last
 
 
+@_on_stream
 def ssm_gdn2_fwd(q, k, v, g, b, w, S0=None, *, scale=1.0, return_state=True, o=None, stream=None,
                  timing=None):
     """Gated DeltaNet-2 forward (the gated delta rule with per-key-dimension decay,
@@ -339,6 +367,7 @@ def ssm_gdn2_fwd(q, k, v, g, b, w, S0=None, *, scale=1.0, return_state=True, o=N
     return o, S_last
 
 
+@_on_stream
 def ssm_conv1d_bwd(x, w, bias, dy, ring0=None, *, want_dring0=False, stream=None, timing=None, out=None):
     """Backward of ssm_conv1d_fwd for the loss sum(dy * y).  Returns a dict with dx
     (io dtype), dw [d_inner, d_conv], dbias [d_inner] and dring0 (float32; None
@@ -368,6 +397,7 @@ def ssm_conv1d_bwd(x, w, bias, dy, ring0=None, *, want_dring0=False, stream=None
     return g
 
 
+@_on_stream
 def ssm_conv1d_step(ring, x, w, bias=None, *, y=None, stream=None, timing=None):
     """One token through the conv ring: ring [batch, d_inner, d_conv-1] float32 is
     updated in place (ignored for d_conv 1); x [batch, d_inner] io dtype.
@@ -479,6 +509,7 @@ def _block_check(X, prm):
     return dm_, pp, dev
 
 
+@_on_stream
 def ssm_block_fwd(ctx, X, params, *, training=True, Y=None, stream=None, timing=None):
     """One Mamba block.  X [batch, L, d_model] (float32 or bfloat16); params: dict
     with W_in [2 d_inner, d_model], W_x [dt_rank + 32, d_inner], W_dt [d_inner,
@@ -503,6 +534,7 @@ def ssm_block_fwd(ctx, X, params, *, training=True, Y=None, stream=None, timing=
     return Y, saved
 
 
+@_on_stream
 def ssm_block_bwd(ctx, X, params, saved, dY, *, out=None, stream=None, timing=None):
     """Backward of ssm_block_fwd for the loss sum(dY * Y).  Returns a dict with dX
     (X's dtype) and d<name> (float32, summed over batch and time) for every

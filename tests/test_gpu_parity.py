@@ -149,41 +149,45 @@ def test_c3_full_length_fd_spot_check():
         assert abs(got - fd) <= F32_GRAD * scale[name], (name, full_idx, got, fd)
 
 
-@pytest.mark.timeout(300)
-def test_c4_mamba2p8b_bf16_sampled():
-    """bf16 I/O at full size.  Per-element outputs, dB and dC checked on batch row 0
-    (all channels); parameter gradients on 64 sampled channels over all rows."""
+def _rel_rows(g, o):
+    """max|g - o| / max|o| over a [batch, ...] tensor, one batch row at a time
+    (bounds host memory at the full-size workloads)."""
+    num = den = 0.0
+    for i in range(o.shape[0]):
+        gi = _np(g[i]) if isinstance(g, torch.Tensor) else np.asarray(g[i], dtype=np.float64)
+        num = max(num, float(np.max(np.abs(gi - o[i]))))
+        den = max(den, float(np.max(np.abs(o[i]))))
+    return num / max(den, 1e-30)
+
+
+@pytest.mark.timeout(600)
+def test_c4_mamba2p8b_bf16_full():
+    """bf16 I/O at full size (batch 4 x 8192 x 5120): every element of every
+    output and gradient against the f64 oracle run on the same bf16 values --
+    y, h_last, dx, ddt, dz, dB, dC on all four batch rows and dA_log, dD,
+    ddt_bias on all 5120 channels.  This covers the multi-block dB/dC partials
+    of every batch row and the parameter partials of every (row, chunk)."""
     inp = W.make_config("c4_mamba2p8b_bf16")
     y, h_last, g = _gpu_fwd_bwd(inp, io=torch.bfloat16)
-    row = {k: inp[k][:1] for k in ("x", "z", "dt", "B", "C", "dy")}
-    row.update({k: inp[k] for k in ("A_log", "D", "dt_bias")})
-    ref = oracle.fwd(row["x"], row["dt"], row["B"], row["C"], row["z"], row["A_log"], row["D"], row["dt_bias"])
-    gr = oracle.bwd(row["x"], row["dt"], row["B"], row["C"], row["z"], row["A_log"], row["D"], row["dt_bias"],
-                    row["dy"])
-    errs = {"y": _rel(y[:1], ref["y"]), "h_last": _rel(h_last[:1], ref["h_last"])}
+    args = [inp[k] for k in ("x", "dt", "B", "C", "z", "A_log", "D", "dt_bias")]
+    ref = oracle.fwd(*args)
+    errs = {"y": _rel_rows(y, ref["y"]), "h_last": _rel_rows(h_last, ref["h_last"])}
+    del ref
+    gr = oracle.bwd(*args, inp["dy"])
     for k in ("dx", "ddt", "dz", "dB", "dC"):
-        errs[k] = _rel(g[k][:1], gr[k])
-    dsel = np.sort(np.random.default_rng(7).choice(inp["x"].shape[2], 64, replace=False))
-    sub = {k: inp[k][:, :, dsel] for k in ("x", "z", "dt", "dy")}
-    sub.update({k: inp[k] for k in ("B", "C")})
-    sub.update({"A_log": inp["A_log"][dsel], "D": inp["D"][dsel], "dt_bias": inp["dt_bias"][dsel]})
-    gp = oracle.bwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"], sub["A_log"], sub["D"], sub["dt_bias"],
-                    sub["dy"])
-    ds = torch.from_numpy(dsel).to(DEV)
+        errs[k] = _rel_rows(g[k], gr[k])
     for k in ("dA_log", "dD", "ddt_bias"):
-        errs[k] = _rel(g[k][ds], gp[k])
-    errs["dx_all_rows_sampled"] = _rel(g["dx"][:, :, ds], gp["dx"])
-    errs["y_all_rows_sampled"] = _rel(y[:, :, ds], oracle.fwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"],
-                                                              sub["A_log"], sub["D"], sub["dt_bias"])["y"])
+        errs[k] = _rel(g[k], gr[k])
     print("c4 max rel errors:", {k: f"{v:.2e}" for k, v in errs.items()})
     assert all(v <= BF16_TOL for v in errs.values()), errs
 
 
-@pytest.mark.timeout(400)
+@pytest.mark.timeout(600)
 def test_c5_decode_steps_equal_forward():
     """1024 single-token steps from a zero state at batch 256 x d_inner 5120:
     bit-identical to the full-sequence forward (which runs its sequence in one
-    chunk at this width) and within 1e-5 of the oracle on 8 batch rows."""
+    chunk at this width), and every y and final state of all 256 batch rows
+    within 1e-5 of the oracle (run 32 rows at a time to bound host memory)."""
     c = W.CONFIGS["c5_decode_step"]
     inp = W.make_config("c5_decode_step", with_dy=False)
     bsz, L, D = inp["x"].shape
@@ -201,13 +205,26 @@ def test_c5_decode_steps_equal_forward():
     for t in range(L):
         ssm.ssm_scan_step(h, xt[t], dtt[t], Bt_[t], Ct_[t], zt[t], A_log, Dp, bias, y=ys[t])
     torch.cuda.synchronize()
+    del xt, zt, dtt, Bt_, Ct_
     assert torch.equal(ys.transpose(0, 1), y_full)
     assert torch.equal(h, h_full)
-    rows = slice(0, 8)
-    ref = oracle.fwd(inp["x"][rows], inp["dt"][rows], inp["B"][rows], inp["C"][rows], inp["z"][rows],
-                     inp["A_log"], inp["D"], inp["dt_bias"])
-    assert _rel(y_full[rows], ref["y"]) <= F32_FWD
-    assert _rel(h[rows], ref["h_last"]) <= F32_FWD
+    del ys
+    num_y = den_y = num_h = den_h = 0.0
+    for r0 in range(0, bsz, 32):
+        rows = slice(r0, min(r0 + 32, bsz))
+        ref = oracle.fwd(inp["x"][rows], inp["dt"][rows], inp["B"][rows], inp["C"][rows], inp["z"][rows],
+                         inp["A_log"], inp["D"], inp["dt_bias"])
+        for i in range(rows.stop - rows.start):
+            gy = _np(y_full[r0 + i])
+            num_y = max(num_y, float(np.max(np.abs(gy - ref["y"][i]))))
+            den_y = max(den_y, float(np.max(np.abs(ref["y"][i]))))
+        gh = _np(h[rows])
+        num_h = max(num_h, float(np.max(np.abs(gh - ref["h_last"]))))
+        den_h = max(den_h, float(np.max(np.abs(ref["h_last"]))))
+        del ref
+    errs = {"y": num_y / den_y, "h": num_h / den_h}
+    print("c5 max rel errors (all 256 rows):", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["y"] <= F32_FWD and errs["h"] <= F32_FWD, errs
     assert c["batch"] == bsz and c["seqlen"] == L
 
 

@@ -55,6 +55,33 @@ def test_scan_on_a_side_stream_matches_default_stream():
     assert torch.equal(y0, y1) and _same(g0, g1)
 
 
+def test_explicit_stream_without_entering_its_context():
+    """stream= passed while another stream is current: the workspace, checkpoints
+    and outputs the binding allocates must belong to the launch stream, so that
+    allocations made meanwhile on the current stream cannot reuse them while the
+    kernels still run.  Busy work on the side stream keeps the kernels in flight
+    while the current stream allocates and fills fresh memory."""
+    t = _scan_inputs()
+    y0, g0 = torch.empty_like(t["x"]), _fresh_grads(t)
+    _scan_step(t, y0, g0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        spin = torch.ones(1 << 24, device=DEV)
+        for _ in range(20):
+            spin.mul_(1.0000001)           # keeps s busy before the scan's kernels
+    y1, ck = ssm.ssm_scan_fwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"],
+                              training=True, stream=s)[0::2]
+    g1 = ssm.ssm_scan_bwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"], ck,
+                          t["dy"], stream=s)
+    for _ in range(8):                     # the current stream allocates and scribbles meanwhile
+        junk = torch.empty(1 << 22, dtype=torch.uint8, device=DEV)
+        junk.fill_(0xFF)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and _same(g0, g1)
+
+
 def test_scan_fwd_bwd_graph_replays_equal_eager():
     t = _scan_inputs()
     y_ref, g_ref = torch.empty_like(t["x"]), _fresh_grads(t)
