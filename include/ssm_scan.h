@@ -115,9 +115,7 @@ enum {
     SSM_K_CONV_STEP = 14,    /* one token through the conv ring */
     SSM_K_CONV_RING = 15,    /* ring copies/fills when seqlen == 0 */
     SSM_K_BLOCK_BC = 16,     /* x_proj's B/C columns split / joined (ssm_block.h) */
-    SSM_K_GDN2_FWD = 17,     /* Gated DeltaNet-2 forward recurrence (ssm_gdn2.h) */
-    SSM_K_TILE_INIT = 18,    /* zeroes the tile tickets/flags, writes the A*log2(e) table */
-    SSM_K_FWD_TILE = 19      /* tiled forward: segments in registers, chained tile carries */
+    SSM_K_GDN2_FWD = 17      /* Gated DeltaNet-2 forward recurrence (ssm_gdn2.h) */
 };
 
 /* Name of a kernel id (for matching profiler output); "?" if unknown. */

@@ -1017,7 +1017,7 @@ const char* ssm_status_str(ssm_status s) {
         case SSM_E_LAUNCH: return "kernel launch failed";
         case SSM_E_UNSUPPORTED:
             return "unsupported configuration (outside the limits its header states: e.g. d_state 16, "
-                   "d_conv 1..4, batch <= 65535, GDN2 k_dim 16/32/64/128 in f32)";
+                   "d_conv 1..4, batch <= 65535, GDN2 k_dim 16/32/64/128)";
     }
     return "unknown status";
 }
