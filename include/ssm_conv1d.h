@@ -77,6 +77,29 @@ ssm_status ssm_conv1d_bwd(const ssm_conv_dims *dims, const void *x, const float 
                           float *dw, float *dbias, float *dring0, void *ws, size_t ws_bytes,
                           hipStream_t stream, ssm_timing *timing);
 
+/* ssm_conv1d_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, allocation-free serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results (bit for bit) as
+ * ssm_conv1d_bwd, except that its per-tile dw/dbias partials go to a static
+ * device buffer of SSM_CONV1D_SCRATCH_BYTES that the library owns instead of a
+ * caller workspace: it calls no hipMalloc, hipFree or allocating routine.
+ *   - Limit: ssm_conv1d_bwd_workspace_bytes(dims) <= SSM_CONV1D_SCRATCH_BYTES
+ *     (16 MiB; the batch 4 x 8192 x 5120, width 4 backward needs 13.1 MB), else
+ *     SSM_E_WORKSPACE and nothing is launched.
+ *   - The buffer lives on the device current on the calling thread when the
+ *     call is made (which must be the stream's device); each GPU holds its own
+ *     copy until the process ends.  Its address is looked up once per device
+ *     (SSM_E_LAUNCH if that lookup fails).
+ *   - Every call on a GPU shares that GPU's buffer and leaves its partials in
+ *     it: calls that overlap on one GPU (streams not ordered with each other)
+ *     race.  Order them on one stream or with events.  Nothing in the buffer
+ *     needs to start at zero: each call writes every partial it reads. */
+#define SSM_CONV1D_SCRATCH_BYTES ((size_t)16 << 20)
+ssm_status ssm_conv1d_bwd_noalloc(const ssm_conv_dims *dims, const void *x, const float *w,
+                                  const float *bias, const float *ring0, const void *dy, void *dx,
+                                  float *dw, float *dbias, float *dring0, hipStream_t stream,
+                                  ssm_timing *timing);
+
 /* One token: y = silu(bias + sum_{k<K-1} w[k]*ring[k] + w[K-1]*x), then the ring
  * drops its oldest entry and appends x (in place).  x, y: [Bt, D] io dtype;
  * ring: [Bt, D, K-1] f32 (may be NULL when K = 1). */

@@ -87,6 +87,8 @@ def _load_library():
     lib.ssm_conv1d_fwd.restype = ctypes.c_int
     lib.ssm_conv1d_bwd.argtypes = [CP] + [P] * 9 + [P, SZ, P, TP]
     lib.ssm_conv1d_bwd.restype = ctypes.c_int
+    lib.ssm_conv1d_bwd_noalloc.argtypes = [CP] + [P] * 9 + [P, TP]
+    lib.ssm_conv1d_bwd_noalloc.restype = ctypes.c_int
     lib.ssm_conv1d_step.argtypes = [I64, I64, I64, I32] + [P] * 5 + [P, TP]
     lib.ssm_conv1d_step.restype = ctypes.c_int
     lib.ssm_gdn2_fwd.argtypes = [ctypes.POINTER(Gdn2Dims)] + [P] * 7 + [ctypes.c_float, P, P, P, TP]
@@ -397,6 +399,34 @@ def ssm_conv1d_bwd(x, w, bias, dy, ring0=None, *, want_dring0=False, stream=None
     return g
 
 
+CONV1D_SCRATCH_BYTES = 16 << 20
+
+
+def ssm_conv1d_bwd_noalloc(x, w, bias, dy, ring0=None, *, dx, dw, dbias, dring0=None, stream=None,
+                           timing=None):
+    """ssm_conv1d_bwd without a workspace: its partials go to the library's static
+    16 MiB device scratch, so the call allocates nothing (every output is the
+    caller's).  Calls that overlap on one GPU share that scratch and race."""
+    dev = x.device
+    bsz, L, din = x.shape
+    io = x.dtype
+    k = w.shape[1] if w.dim() == 2 else -1
+    _check(x, "x", (bsz, L, din), io, dev)
+    _check(dy, "dy", (bsz, L, din), io, dev)
+    _check(w, "w", (din, k), torch.float32, dev)
+    _check(bias, "bias", (din,), torch.float32, dev, required=False)
+    ring0 = _ring(ring0, "ring0", bsz, din, k, dev)
+    _check(dx, "dx", (bsz, L, din), io, dev)
+    _check(dw, "dw", (din, k), torch.float32, dev)
+    _check(dbias, "dbias", (din,), torch.float32, dev)
+    dring0 = _ring(dring0, "dring0", bsz, din, k, dev)
+    dm = conv_dims(bsz, L, din, k, io)
+    rc = _lib.ssm_conv1d_bwd_noalloc(ctypes.byref(dm), _ptr(x), _ptr(w), _ptr(bias), _ptr(ring0), _ptr(dy),
+                                     _ptr(dx), _ptr(dw), _ptr(dbias), _ptr(dring0), _stream(dev, stream),
+                                     _timing_ptr(timing))
+    _raise("ssm_conv1d_bwd_noalloc", rc)
+
+
 @_on_stream
 def ssm_conv1d_step(ring, x, w, bias=None, *, y=None, stream=None, timing=None):
     """One token through the conv ring: ring [batch, d_inner, d_conv-1] float32 is
@@ -609,5 +639,5 @@ class LaunchTimer:
 __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_scan_step", "ckpt_bytes", "fwd_workspace_bytes",
            "bwd_workspace_bytes", "LaunchTimer", "SsmError", "library", "status_str", "kernel_name",
            "SsmDims", "SsmTiming", "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_conv1d_step",
-           "conv1d_bwd_workspace_bytes", "ConvDims", "BlockContext", "ssm_block_fwd", "ssm_block_bwd",
+           "conv1d_bwd_workspace_bytes", "ConvDims", "ssm_conv1d_bwd_noalloc", "CONV1D_SCRATCH_BYTES", "BlockContext", "ssm_block_fwd", "ssm_block_bwd",
            "block_library", "BlockDims", "ssm_gdn2_fwd", "Gdn2Dims"]

@@ -29,6 +29,7 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "ssm_common.h"
@@ -572,6 +573,31 @@ ssm_status dispatch(const ConvPlan& p, F&& f) {
 
 }  // namespace
 
+// Scratch of ssm_conv1d_bwd_noalloc: each GPU the library runs on holds one
+// copy, at its own device address.  Host code never uses this name as an
+// address (on the host it is a stand-in): the per-device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+__device__ __align__(256) unsigned char scratch[SSM_CONV1D_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES];  // device address of `scratch`, per device
+
+ssm_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SSM_E_LAUNCH;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSM_E_LAUNCH;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return SSM_OK;
+}
+}  // namespace
+
 extern "C" {
 
 size_t ssm_conv1d_bwd_workspace_bytes(const ssm_conv_dims* dims) {
@@ -634,6 +660,18 @@ ssm_status ssm_conv1d_bwd(const ssm_conv_dims* dims, const void* x, const float*
     float* part = static_cast<float*>(ws);
     BwdCall f{p, x, w, bias, ring0, dy, dx, dw, dbias, dring0, part, launch};
     return dispatch(p, f);
+}
+
+ssm_status ssm_conv1d_bwd_noalloc(const ssm_conv_dims* dims, const void* x, const float* w,
+                                  const float* bias, const float* ring0, const void* dy, void* dx,
+                                  float* dw, float* dbias, float* dring0, hipStream_t stream,
+                                  ssm_timing* timing) {
+    SSM_TRY(check_conv(dims));
+    const size_t need = dims->seqlen > 0 ? conv_ws_bytes(conv_plan(dims)) : 0;
+    if (need > SSM_CONV1D_SCRATCH_BYTES) return SSM_E_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) SSM_TRY(scratch_on_current_device(&ws));
+    return ssm_conv1d_bwd(dims, x, w, bias, ring0, dy, dx, dw, dbias, dring0, ws, need, stream, timing);
 }
 
 ssm_status ssm_conv1d_step(int64_t batch, int64_t d_inner, int64_t d_conv, int32_t io_dtype,
