@@ -63,6 +63,8 @@ def parse():
                          "decode: 1024 single-token steps at batch 256 x d_inner 5120, eager and "
                          "replayed from a captured HIP graph; block: one Mamba block (projections on "
                          "hipBLASLt around the conv and the scan) fwd+bwd at the 2.8B layer shape")
+    ap.add_argument("--gdn2-form", choices=("chunked", "recurrent"), default="chunked",
+                    help="--op gdn2: the chunked WY form on MFMA or the token recurrence")
     ap.add_argument("--dim", type=int, default=16,
                     help="--op train: d_model of the one-block model (d_inner = 2 d_model)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -513,9 +515,13 @@ def train_bench(args):
             f.write(out + "\n")
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
 def gdn2_bench(args):
     """Gated DeltaNet-2 forward over batch 4 x 16 heads x 4096 tokens, k_dim =
-    v_dim = 128, f32 (inputs resident on the GPU)."""
+    v_dim = 128, f32 (inputs resident on the GPU): the chunked WY form on MFMA
+    (default) or, with --gdn2-form recurrent, the token recurrence."""
     import math
 
     import numpy as np
@@ -527,6 +533,7 @@ def gdn2_bench(args):
     name = "gdn2_b4h16t4096"
     c = W.GDN2_CONFIGS[name]
     B, H, L, K, V = c["batch"], c["heads"], c["seqlen"], c["k_dim"], c["v_dim"]
+    chunked = args.gdn2_form == "chunked"
     dev = torch.device("cuda:0")
     print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
     inp = W.make_gdn2_config(name)
@@ -534,9 +541,10 @@ def gdn2_bench(args):
     t = {n: torch.from_numpy(inp[n]).to(dev) for n in names}
     scale = 1.0 / math.sqrt(K)
     o = torch.empty(B, H, L, V, dtype=torch.float32, device=dev)
+    fwd = ssm.ssm_gdn2_fwd_chunked if chunked else ssm.ssm_gdn2_fwd
 
     def step(timer=None):
-        ssm.ssm_gdn2_fwd(*[t[n] for n in names], None, scale=scale, o=o, timing=timer)
+        fwd(*[t[n] for n in names], None, scale=scale, o=o, return_state=False, timing=timer)
 
     if args.copy_probe:
         copy_probe(dev)
@@ -552,26 +560,47 @@ def gdn2_bench(args):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    kms = float(np.mean([km for tm in timers for _, km in tm.results()]))
+    per = {}
     for tm in timers:
+        for kn, km in tm.results():
+            per.setdefault(kn, []).append(km)
         tm.close()
+    kavg = {kn: float(np.mean(v)) for kn, v in per.items()}
     ht = B * H * L                       # head-tokens
-    flops = 7.0 * K * V * ht             # decay mul, erase-read, write and output FMAs per state element
     nbytes = 4.0 * (4 * K + 3 * V) * ht  # q, k, g, b read; v, w read; o written (f32)
-    tflops = flops / (kms * 1e-3) / 1e12
+    if chunked:
+        # MFMA work of the state pass as issued: per 64-token chunk and 16 columns,
+        # 16x16x4 products for -BKe S and Qe S (4 K/4 each), M^-1 X and P vn (the 40
+        # lower-triangular tiles each) and Kd^T vn (K/16 x 16), 2048 flops each
+        dom = "k_gdn2_state"
+        mfmas = (8 * (K // 4) + 80 + K) * (L // 64) * (V // 16) * B * H
+        flops = 2048.0 * mfmas
+        tflops = flops / (kavg[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "kernel_ms": round(kavg[dom], 4), "flops_per_launch": flops,
+                "note": "f32 MFMA (v_mfma_f32_16x16x4f32) work of the state pass as issued"}
+        form = "chunked WY form, 64-token chunks, products on MFMA"
+    else:
+        dom = "k_gdn2_fwd"
+        flops = 7.0 * K * V * ht  # decay mul, erase-read, write and output FMAs per state element
+        tflops = flops / (kavg[dom] * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(tflops, 2), "peak": 78.6, "unit": "TFLOP/s",
+                "frac": round(tflops / 78.6, 4), "traffic": measured_traffic("k_gdn2_fwd", "gdn2"), "kernel": dom,
+                "kernel_ms": round(kavg[dom], 4),
+                "note": "f32 vector FMA peak without packed math (256 CUs x 64 lanes x 2 flops x 2.4 GHz)"}
+        form = "token-by-token recurrence"
     line = {
         "metric": "GDN2 forward tokens/s", "value": B * L / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{name}: batch={B} heads={H} seqlen={L} k_dim={K} v_dim={V}, f32, forward "
-                               f"(gated delta rule, token-by-token recurrence)",
+                               f"(gated delta rule, {form})",
                    "batch": B, "heads": H, "seqlen": L, "k_dim": K, "v_dim": V},
-        "kernels_ms": {"k_gdn2_fwd": round(kms, 4)},
-        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": F32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / F32_VECTOR_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("k_gdn2_fwd", "gdn2"), "kernel": "k_gdn2_fwd"},
-        "roofline_hbm": {"bound": "hbm", "achieved": round(nbytes / (kms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(nbytes / (kms * 1e-3) / 8e12, 4)},
+        "kernels_ms": {kn: round(v, 4) for kn, v in sorted(kavg.items())},
+        "roofline": roof,
+        "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "frac": round(nbytes / (ms * 1e-3) / 8e12, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -585,7 +614,7 @@ def gdn2_bench(args):
         line["cpu_baseline"] = {"value": Ls / H / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
                                 "kind": "oracle",
                                 "sample": f"batch 0, head 0, the first {Ls} tokens in f64 ({sec:.1f} s), scaled "
-                                          f"to all {H} heads of a token"}
+                                          f"to all {H} heads of a token", **host_cpu()}
     out = json.dumps(line)
     print(out, flush=True)
     if args.out:

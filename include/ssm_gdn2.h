@@ -51,6 +51,32 @@ ssm_status ssm_gdn2_fwd(const ssm_gdn2_dims *dims, const void *q, const void *k,
                         const void *g, const void *b, const void *w, const float *S0, float scale,
                         void *o, float *S_last, hipStream_t stream, ssm_timing *timing);
 
+/* The same forward in chunks of 64 tokens: the WY form of the page's chunked
+ * forward with the decays kept per key dimension, its products on MFMA
+ * (v_mfma_f32_16x16x4f32, f32).  Per chunk, with G the inclusive cumulative sum
+ * of g inside the chunk:
+ *     A[i][j] = sum_k b_i k_i k_j exp(G_i - G_j)  (j < i),  M = I + A
+ *     P[i][j] = sum_k q_i k_j exp(G_i - G_j)      (j <= i)
+ *     vn = M^{-1} (w*v - (b*k*exp(G)) S),  o = scale (P vn + (q*exp(G)) S)
+ *     S  = diag(exp(G_last)) S + (k*exp(G_last - G))^T vn
+ * Every exp(G_i - G_j) is formed per element with i >= j (<= 1 for g <= 0), so
+ * strongly gated heads cannot overflow it.  Equal to ssm_gdn2_fwd up to f32
+ * rounding (not bit for bit).  Chaining calls through S_last -> S0 reproduces
+ * one call over the joined sequence bit for bit when every call but the last
+ * has a multiple of 64 tokens (the chunk grouping is then the same).
+ *   - Same arguments and layouts as ssm_gdn2_fwd, plus a caller-owned
+ *     workspace of ssm_gdn2_chunked_workspace_bytes(dims) bytes (per pair and
+ *     chunk: 192 k_dim + 8192 + k_dim floats, rounded up to 64), overwritten.
+ *   - Limits: k_dim in {16, 32, 64, 128}, v_dim a multiple of 16
+ *     (SSM_E_UNSUPPORTED otherwise; ssm_gdn2_fwd takes any v_dim);
+ *     batch*heads and the chunk count at most 65535.
+ *   - seqlen 0 writes S_last = S0 (zeros when S0 is NULL); ws may be NULL. */
+size_t ssm_gdn2_chunked_workspace_bytes(const ssm_gdn2_dims *dims);
+ssm_status ssm_gdn2_fwd_chunked(const ssm_gdn2_dims *dims, const void *q, const void *k,
+                                const void *v, const void *g, const void *b, const void *w,
+                                const float *S0, float scale, void *o, float *S_last, void *ws,
+                                size_t ws_bytes, hipStream_t stream, ssm_timing *timing);
+
 #ifdef __cplusplus
 }
 #endif

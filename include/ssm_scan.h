@@ -115,7 +115,9 @@ enum {
     SSM_K_CONV_STEP = 14,    /* one token through the conv ring */
     SSM_K_CONV_RING = 15,    /* ring copies/fills when seqlen == 0 */
     SSM_K_BLOCK_BC = 16,     /* x_proj's B/C columns split / joined (ssm_block.h) */
-    SSM_K_GDN2_FWD = 17      /* Gated DeltaNet-2 forward recurrence (ssm_gdn2.h) */
+    SSM_K_GDN2_FWD = 17,     /* Gated DeltaNet-2 forward recurrence (ssm_gdn2.h) */
+    SSM_K_GDN2_WY = 18,      /* GDN2 chunked form: key side per chunk (decays, A, P, M^-1) */
+    SSM_K_GDN2_STATE = 19    /* GDN2 chunked form: state pass over the chunks (MFMA) */
 };
 
 /* Name of a kernel id (for matching profiler output); "?" if unknown. */

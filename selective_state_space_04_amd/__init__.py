@@ -93,6 +93,10 @@ def _load_library():
     lib.ssm_conv1d_step.restype = ctypes.c_int
     lib.ssm_gdn2_fwd.argtypes = [ctypes.POINTER(Gdn2Dims)] + [P] * 7 + [ctypes.c_float, P, P, P, TP]
     lib.ssm_gdn2_fwd.restype = ctypes.c_int
+    lib.ssm_gdn2_chunked_workspace_bytes.argtypes = [ctypes.POINTER(Gdn2Dims)]
+    lib.ssm_gdn2_chunked_workspace_bytes.restype = SZ
+    lib.ssm_gdn2_fwd_chunked.argtypes = [ctypes.POINTER(Gdn2Dims)] + [P] * 7 + [ctypes.c_float, P, P, P, SZ, P, TP]
+    lib.ssm_gdn2_fwd_chunked.restype = ctypes.c_int
     return lib
 
 
@@ -369,6 +373,40 @@ def ssm_gdn2_fwd(q, k, v, g, b, w, S0=None, *, scale=1.0, return_state=True, o=N
     return o, S_last
 
 
+def gdn2_chunked_workspace_bytes(batch, heads, seqlen, k_dim, v_dim, io_dtype=torch.float32):
+    dm = Gdn2Dims(int(batch), int(heads), int(seqlen), int(k_dim), int(v_dim), _io_code(io_dtype))
+    return int(_lib.ssm_gdn2_chunked_workspace_bytes(ctypes.byref(dm)))
+
+
+@_on_stream
+def ssm_gdn2_fwd_chunked(q, k, v, g, b, w, S0=None, *, scale=1.0, return_state=True, o=None, stream=None,
+                         timing=None):
+    """The Gated DeltaNet-2 forward in chunks of 64 tokens (WY form, decays per key
+    dimension, products on MFMA); same arguments and results as ssm_gdn2_fwd up to
+    f32 rounding.  v_dim must be a multiple of 16."""
+    dev = q.device
+    io = q.dtype
+    bsz, nh, L, kd = q.shape
+    vd = v.shape[-1] if v.dim() == 4 else -1
+    for t, n in ((q, "q"), (k, "k"), (g, "g"), (b, "b")):
+        _check(t, n, (bsz, nh, L, kd), io, dev)
+    for t, n in ((v, "v"), (w, "w")):
+        _check(t, n, (bsz, nh, L, vd), io, dev)
+    _check(S0, "S0", (bsz, nh, kd, vd), torch.float32, dev, required=False)
+    if o is None:
+        o = torch.empty(bsz, nh, L, vd, dtype=io, device=dev)
+    _check(o, "o", (bsz, nh, L, vd), io, dev)
+    S_last = torch.empty(bsz, nh, kd, vd, dtype=torch.float32, device=dev) if return_state else None
+    dm = Gdn2Dims(bsz, nh, L, kd, vd, _io_code(io))
+    nws = _lib.ssm_gdn2_chunked_workspace_bytes(ctypes.byref(dm))
+    ws = _workspace(nws, dev)
+    rc = _lib.ssm_gdn2_fwd_chunked(ctypes.byref(dm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                                   _ptr(S0), float(scale), _ptr(o), _ptr(S_last), _ptr(ws), nws,
+                                   _stream(dev, stream), _timing_ptr(timing))
+    _raise("ssm_gdn2_fwd_chunked", rc)
+    return o, S_last
+
+
 @_on_stream
 def ssm_conv1d_bwd(x, w, bias, dy, ring0=None, *, want_dring0=False, stream=None, timing=None, out=None):
     """Backward of ssm_conv1d_fwd for the loss sum(dy * y).  Returns a dict with dx
@@ -640,4 +678,5 @@ __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_scan_step", "ckpt_bytes", "fwd_w
            "bwd_workspace_bytes", "LaunchTimer", "SsmError", "library", "status_str", "kernel_name",
            "SsmDims", "SsmTiming", "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_conv1d_step",
            "conv1d_bwd_workspace_bytes", "ConvDims", "ssm_conv1d_bwd_noalloc", "CONV1D_SCRATCH_BYTES", "BlockContext", "ssm_block_fwd", "ssm_block_bwd",
-           "block_library", "BlockDims", "ssm_gdn2_fwd", "Gdn2Dims"]
+           "block_library", "BlockDims", "ssm_gdn2_fwd", "Gdn2Dims", "ssm_gdn2_fwd_chunked",
+           "gdn2_chunked_workspace_bytes"]

@@ -6,7 +6,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", n) for n in ("ssm_scan.hip", "ssm_conv1d.hip", "ssm_gdn2.hip")]
+SRCS = [os.path.join(HERE, "csrc", n)
+        for n in ("ssm_scan.hip", "ssm_conv1d.hip", "ssm_gdn2.hip", "ssm_gdn2_chunk.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libssmscan.so")
 BLOCK_SRC = os.path.join(HERE, "csrc", "ssm_block.hip")

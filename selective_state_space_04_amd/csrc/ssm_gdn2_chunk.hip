@@ -1,0 +1,429 @@
+// ssm_gdn2_chunk.hip -- Gated DeltaNet-2 forward in chunks of 64 tokens for
+// MI355X (gfx950): the chunked WY form of burn-gdn2 0.1.4, page
+// "src/forward.rs", with the decays kept per key dimension (the per-token
+// recurrence it regroups is in ssm_gdn2.h).
+//
+// Per (batch*head pair, chunk of CH tokens), with G the inclusive cumulative
+// sum of the log-decays g inside the chunk ([CH, K]) and S the [K, V] state
+// entering the chunk:
+//   A[i][j] = sum_k b_i k_i k_j exp(G_i - G_j)        (j < i)
+//   P[i][j] = sum_k q_i k_j exp(G_i - G_j)            (j <= i)
+//   M = I + A,  BKe = b * k * exp(G),  Qe = q * exp(G),  Kd = k * exp(G_last - G)
+//   vn = M^{-1} (w * v - BKe S)          (the corrected values)
+//   o  = scale (P vn + Qe S)
+//   S' = diag(exp(G_last)) S + Kd^T vn
+// Every exp(G_i - G_j) used has i >= j, so it is <= 1 for log-decays <= 0: the
+// decays are formed directly per element, never split into exp(G_i) and
+// exp(-G_j), so no gate strength can overflow them.
+//
+// Two kernels:
+//   k_gdn2_wy     key side, parallel over (pair, chunk): G, A and P (VALU, the
+//                 exp per element), M^{-1} by forward substitution, BKe, Qe,
+//                 Kd, exp(G_last); everything written to the workspace in the
+//                 operand order of v_mfma_f32_16x16x4f32.
+//   k_gdn2_state  one wave per (pair, 16 state columns), sequential over the
+//                 chunks: the five products above on MFMA, the state in
+//                 registers.  The 16 columns of a pair run on one XCD, so its L2
+//                 serves their shared key-side reads.
+// MFMA lane layout (v_mfma_f32_16x16x4f32, one wave): A[i][k] comes from lane
+// 16k + i, B[k][j] from lane 16k + j, and D[4q + r][j] lands in lane 16q + j,
+// register r.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssm_common.h"
+#include "ssm_gdn2.h"
+
+namespace {
+
+constexpr int CH = 64;       // tokens per chunk
+constexpr int WGK = 256;     // threads of the key-side kernel
+constexpr int NBLK = 136;    // 4x4 blocks of the lower triangle of a CH x CH matrix
+constexpr int XCDS = 8;
+constexpr float LOG2E = 1.4426950408889634f;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Workspace per (pair, chunk), in floats, for key dimension K.
+template <int K>
+struct Lay {
+    // A operands, four consecutive contraction blocks per lane as one float4:
+    // element (tile, block m, lane) at ((tile * nblocks / 4 + m / 4) * 64 + lane) * 4 + m % 4
+    static constexpr int nBKe = 0;                 // -BKe:   [4 row tiles][K/4 k-blocks]
+    static constexpr int Qe = nBKe + CH * K;       // Qe:     [4][K/4]
+    static constexpr int KdT = Qe + CH * K;        // Kd^T:   [K/16 row tiles][16 token blocks]
+    static constexpr int P = KdT + CH * K;         // P:      [4][16]
+    static constexpr int Mi = P + CH * CH;         // M^{-1}: [4][16]
+    static constexpr int eGl = Mi + CH * CH;       // exp(G_last):       [K]
+    static constexpr int total = (eGl + K + 63) / 64 * 64;
+};
+
+template <typename TT>
+__device__ __forceinline__ float ld(const TT* p, int64_t i) { return ssm::to_f(p[i]); }
+
+// Offset of A-operand element (tile, contraction block m, lane) in a region
+// whose tiles have nb blocks each.
+__host__ __device__ constexpr int aop(int tile, int m, int lane, int nb) {
+    return ((tile * (nb / 4) + m / 4) * 64 + lane) * 4 + m % 4;
+}
+
+// Key side of one chunk.  grid (chunks, pairs), WGK threads.
+template <typename TT, int K>
+__global__ __launch_bounds__(WGK) void k_gdn2_wy(const TT* __restrict__ q, const TT* __restrict__ k,
+                                                 const TT* __restrict__ g, const TT* __restrict__ b,
+                                                 float* __restrict__ ws, int T, int nch) {
+    constexpr int KC = K < 32 ? K : 32;  // key dimensions staged per pass
+    using L = Lay<K>;
+    __shared__ float Gs[KC][CH], ks[KC][CH], bks[KC][CH], qs[KC][CH];
+    __shared__ float As[CH][CH], Ps[CH][CH], Ms[CH][CH];
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x;
+    const int64_t pair = blockIdx.y;
+    const int t0 = c * CH;
+    const int n = min(CH, T - t0);
+    float* out = ws + (pair * nch + c) * (int64_t)L::total;
+    const int64_t row0 = pair * T + t0;
+    for (int e = tid; e < CH * CH; e += WGK) {
+        (&As[0][0])[e] = 0.0f;
+        (&Ps[0][0])[e] = 0.0f;
+    }
+    // this thread's 4x4 block (bi, bj), bj <= bi, of A and P
+    int bi = 0, bj = tid;
+    while (bj > bi) {
+        bj -= bi + 1;
+        ++bi;
+    }
+    const bool blk = tid < NBLK;
+    float Aa[4][4], Pa[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) Aa[a][cc] = Pa[a][cc] = 0.0f;
+    for (int kc = 0; kc < K / KC; ++kc) {
+        for (int e = tid; e < CH * KC; e += WGK) {
+            const int tok = e / KC, kl = e % KC;
+            const bool valid = tok < n;
+            const int64_t src = (row0 + tok) * K + kc * KC + kl;
+            const float kv = valid ? ld(k, src) : 0.0f;
+            ks[kl][tok] = kv;
+            bks[kl][tok] = valid ? ld(b, src) * kv : 0.0f;
+            qs[kl][tok] = valid ? ld(q, src) : 0.0f;
+            Gs[kl][tok] = valid ? ld(g, src) : 0.0f;  // a padded token is the identity: g = 0
+        }
+        __syncthreads();
+        if (tid < KC) {  // inclusive cumulative sum over the chunk's tokens (in registers)
+            float gv[CH];
+#pragma unroll
+            for (int tok = 0; tok < CH; ++tok) gv[tok] = Gs[tid][tok];
+#pragma unroll
+            for (int tok = 1; tok < CH; ++tok) gv[tok] += gv[tok - 1];
+#pragma unroll
+            for (int tok = 0; tok < CH; ++tok) Gs[tid][tok] = gv[tok];
+        }
+        __syncthreads();
+        if (blk) {
+            for (int kl = 0; kl < KC; ++kl) {
+                const f4 gi = *reinterpret_cast<const f4*>(&Gs[kl][4 * bi]);
+                const f4 gj = *reinterpret_cast<const f4*>(&Gs[kl][4 * bj]);
+                const f4 kj = *reinterpret_cast<const f4*>(&ks[kl][4 * bj]);
+                const f4 bki = *reinterpret_cast<const f4*>(&bks[kl][4 * bi]);
+                const f4 qi = *reinterpret_cast<const f4*>(&qs[kl][4 * bi]);
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) {
+                        // entries with j > i (upper part of a diagonal block) are
+                        // masked below; their exponent is zeroed so it stays finite
+                        const bool upper = bi == bj && cc > a;
+                        const float dec = __builtin_amdgcn_exp2f(upper ? 0.0f : (gi[a] - gj[cc]) * LOG2E);
+                        const float kd = kj[cc] * dec;
+                        Aa[a][cc] = __builtin_fmaf(bki[a], kd, Aa[a][cc]);
+                        Pa[a][cc] = __builtin_fmaf(qi[a], kd, Pa[a][cc]);
+                    }
+            }
+        }
+        // the chunk's operands for these KC key dimensions
+        for (int e = tid; e < CH * KC; e += WGK) {
+            const int ti = e / (KC * 16), rem = e % (KC * 16), ml = rem / 64, ln = rem % 64;
+            const int tok = 16 * ti + ln % 16, kl = 4 * ml + ln / 16;
+            const float eg = __builtin_amdgcn_exp2f(Gs[kl][tok] * LOG2E);
+            const int o = aop(ti, kc * (KC / 4) + ml, ln, K / 4);
+            out[L::nBKe + o] = -bks[kl][tok] * eg;
+            out[L::Qe + o] = qs[kl][tok] * eg;
+        }
+        for (int e = tid; e < CH * KC; e += WGK) {
+            const int tkl = e / (16 * 64), rem = e % (16 * 64), mj = rem / 64, ln = rem % 64;
+            const int tok = 4 * mj + ln / 16, kl = 16 * tkl + ln % 16;
+            const float dec = __builtin_amdgcn_exp2f((Gs[kl][CH - 1] - Gs[kl][tok]) * LOG2E);
+            out[L::KdT + aop(kc * (KC / 16) + tkl, mj, ln, 16)] = ks[kl][tok] * dec;
+        }
+        if (tid < KC) out[L::eGl + kc * KC + tid] = __builtin_amdgcn_exp2f(Gs[tid][CH - 1] * LOG2E);
+        __syncthreads();
+    }
+    if (blk) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const int i = 4 * bi + a, j = 4 * bj + cc;
+                As[i][j] = j < i ? Aa[a][cc] : 0.0f;
+                Ps[i][j] = j <= i ? Pa[a][cc] : 0.0f;
+            }
+    }
+    __syncthreads();
+    if (tid < CH) {
+        // column tid of M^{-1}, M = I + A unit lower triangular: forward
+        // substitution X[i] = [i == tid] - sum_{j<i} A[i][j] X[j]
+        // (each row's sum is split over j mod 4 into four chains, added in a
+        // fixed order)
+        float X[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            float s4[4] = {i == tid ? 1.0f : 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < i; ++j) s4[j & 3] = __builtin_fmaf(-As[i][j], X[j], s4[j & 3]);
+            const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            X[i] = s;
+            Ms[i][tid] = s;
+        }
+    } else {
+        for (int e = tid - CH; e < CH * CH; e += WGK - CH) {
+            const int ti = e / 1024, mj = (e / 64) % 16, ln = e % 64;
+            out[L::P + aop(ti, mj, ln, 16)] = Ps[16 * ti + ln % 16][4 * mj + ln / 16];
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < CH * CH; e += WGK) {
+        const int ti = e / 1024, mj = (e / 64) % 16, ln = e % 64;
+        out[L::Mi + aop(ti, mj, ln, 16)] = Ms[16 * ti + ln % 16][4 * mj + ln / 16];
+    }
+}
+
+__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Four consecutive A-operand blocks (4 m4 .. 4 m4 + 3) of a tile for this lane.
+__device__ __forceinline__ f4 opnd(const float* region, int tile, int m4, int lane, int nb) {
+    return *reinterpret_cast<const f4*>(region + ((tile * (nb / 4) + m4) * 64 + lane) * 4);
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// State pass: one wave per (pair, 16 columns of V).
+template <typename TT, int K>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gdn2_state(const TT* __restrict__ v, const TT* __restrict__ w,
+                                                   const float* __restrict__ ws,
+                                                   const float* __restrict__ S0, float scale,
+                                                   TT* __restrict__ o, float* __restrict__ S_last,
+                                                   int64_t nbh, int64_t nbh8, int T, int V, int nch) {
+    using L = Lay<K>;
+    constexpr int KB = K / 4;  // k-blocks of the state operand
+    __shared__ float xs[CH][17];
+    __shared__ float ss[K][17];
+    const int l = threadIdx.x;
+    const int64_t pair = blockIdx.x % nbh8;  // a pair's column blocks share blockIdx % 8, hence an XCD
+    const int cb = (int)(blockIdx.x / nbh8);
+    if (pair >= nbh) return;
+    const int col = cb * 16 + (l & 15);
+    const int quad = l >> 4;
+    // the state as the B operand of the k-contractions: Skb[m] = S[4m + quad][col]
+    float Skb[KB];
+#pragma unroll
+    for (int m = 0; m < KB; ++m) Skb[m] = S0 ? S0[(pair * K + 4 * m + quad) * V + col] : 0.0f;
+    // The chunk body is one branch-free block (clamped, masked loads; the o
+    // stores at its end), so that operand loads can be scheduled ahead of the
+    // MFMAs that consume them.
+    for (int c = 0; c < nch; ++c) {
+        const float* base = ws + (pair * nch + c) * (int64_t)L::total;
+        const int t0 = c * CH;
+        // X = w * v - BKe S and the state part of the output, oq = Qe S: both
+        // contract S over the key dimension, so they share its operand blocks
+        f4 X[4], oq[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = t0 + 16 * ti + 4 * quad + r;
+                const int64_t e = (pair * T + min(tok, T - 1)) * V + col;
+                X[ti][r] = tok < T ? ld(w, e) * ld(v, e) : 0.0f;
+                oq[ti][r] = 0.0f;
+            }
+#pragma unroll
+        for (int m4 = 0; m4 < KB / 4; ++m4) {
+            f4 ax[4], aq[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                ax[ti] = opnd(base + L::nBKe, ti, m4, l, KB);
+                aq[ti] = opnd(base + L::Qe, ti, m4, l, KB);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    X[ti] = mfma(ax[ti][u], Skb[4 * m4 + u], X[ti]);
+                    oq[ti] = mfma(aq[ti][u], Skb[4 * m4 + u], oq[ti]);
+                }
+        }
+        // X as the B operand of the token contractions
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xs[16 * ti + 4 * quad + r][l & 15] = X[ti][r];
+        wave_sync_lds();
+        float Xkb[16];
+#pragma unroll
+        for (int mj = 0; mj < 16; ++mj) Xkb[mj] = xs[4 * mj + quad][l & 15];
+        // vn = M^{-1} X (lower triangular: token blocks mj <= 4 ti + 3)
+        f4 vn[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) vn[ti] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4)
+#pragma unroll
+            for (int ti = m4; ti < 4; ++ti) {
+                const f4 a = opnd(base + L::Mi, ti, m4, l, 16);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) vn[ti] = mfma(a[u], Xkb[4 * m4 + u], vn[ti]);
+            }
+        wave_sync_lds();
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xs[16 * ti + 4 * quad + r][l & 15] = vn[ti][r];
+        wave_sync_lds();
+        float vkb[16];
+#pragma unroll
+        for (int mj = 0; mj < 16; ++mj) vkb[mj] = xs[4 * mj + quad][l & 15];
+        // o = scale (P vn + Qe S) and S' = diag(exp(G_last)) S + Kd^T vn
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4)
+#pragma unroll
+            for (int ti = m4; ti < 4; ++ti) {
+                const f4 a = opnd(base + L::P, ti, m4, l, 16);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) oq[ti] = mfma(a[u], vkb[4 * m4 + u], oq[ti]);
+            }
+        f4 sn[K / 16];
+#pragma unroll
+        for (int tk = 0; tk < K / 16; ++tk) sn[tk] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4)
+#pragma unroll
+            for (int tk = 0; tk < K / 16; ++tk) {
+                const f4 a = opnd(base + L::KdT, tk, m4, l, 16);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sn[tk] = mfma(a[u], vkb[4 * m4 + u], sn[tk]);
+            }
+#pragma unroll
+        for (int tk = 0; tk < K / 16; ++tk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ss[16 * tk + 4 * quad + r][l & 15] = sn[tk][r];
+        wave_sync_lds();
+#pragma unroll
+        for (int m = 0; m < KB; ++m)
+            Skb[m] = __builtin_fmaf(base[L::eGl + 4 * m + quad], Skb[m], ss[4 * m + quad][l & 15]);
+        wave_sync_lds();
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = t0 + 16 * ti + 4 * quad + r;
+                if (tok < T) o[(pair * T + tok) * V + col] = ssm::from_f<TT>(scale * oq[ti][r]);
+            }
+    }
+    if (S_last) {
+#pragma unroll
+        for (int m = 0; m < KB; ++m) S_last[(pair * K + 4 * m + quad) * V + col] = Skb[m];
+    }
+}
+
+ssm_status check_dims(const ssm_gdn2_dims* d) {
+    if (!d) return SSM_E_NULLPTR;
+    if (d->batch < 1 || d->heads < 1 || d->seqlen < 0 || d->k_dim < 1 || d->v_dim < 1) return SSM_E_SHAPE;
+    if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_E_DTYPE;
+    if (d->k_dim != 16 && d->k_dim != 32 && d->k_dim != 64 && d->k_dim != 128) return SSM_E_UNSUPPORTED;
+    if (d->v_dim % 16 != 0) return SSM_E_UNSUPPORTED;
+    const int64_t nbh = d->batch * d->heads, nch = (d->seqlen + CH - 1) / CH;
+    if (d->batch > 65535 || d->heads > 65535 || d->seqlen > ((int64_t)1 << 30) ||
+        d->v_dim > ((int64_t)1 << 24) || nbh > 65535 || nch > 65535 ||
+        (nbh + XCDS - 1) / XCDS * XCDS * (d->v_dim / 16) >= ((int64_t)1 << 31))
+        return SSM_E_UNSUPPORTED;
+    return SSM_OK;
+}
+
+int64_t chunk_floats(int64_t kd) {
+    switch (kd) {
+        case 16: return Lay<16>::total;
+        case 32: return Lay<32>::total;
+        case 64: return Lay<64>::total;
+        default: return Lay<128>::total;
+    }
+}
+
+size_t ws_bytes_for(const ssm_gdn2_dims* d) {
+    const int64_t nch = (d->seqlen + CH - 1) / CH;
+    return sizeof(float) * (size_t)(d->batch * d->heads * nch * chunk_floats(d->k_dim));
+}
+
+template <typename TT, int K>
+ssm_status run(const ssm_gdn2_dims* d, const void* q, const void* k, const void* v, const void* g,
+               const void* b, const void* w, const float* S0, float scale, void* o, float* S_last,
+               float* ws, ssm::Launcher& launch) {
+    const int64_t nbh = d->batch * d->heads;
+    const int T = (int)d->seqlen, V = (int)d->v_dim;
+    const int nch = (T + CH - 1) / CH;
+    SSM_TRY(launch(SSM_K_GDN2_WY, k_gdn2_wy<TT, K>, dim3((unsigned)nch, (unsigned)nbh), dim3(WGK), (const TT*)q,
+                   (const TT*)k, (const TT*)g, (const TT*)b, ws, T, nch));
+    const int64_t nbh8 = (nbh + XCDS - 1) / XCDS * XCDS;
+    return launch(SSM_K_GDN2_STATE, k_gdn2_state<TT, K>, dim3((unsigned)(nbh8 * (V / 16))), dim3(64), (const TT*)v,
+                  (const TT*)w, (const float*)ws, S0, scale, (TT*)o, S_last, nbh, nbh8, T, V, nch);
+}
+
+template <typename TT>
+ssm_status run_k(const ssm_gdn2_dims* d, const void* q, const void* k, const void* v, const void* g,
+                 const void* b, const void* w, const float* S0, float scale, void* o, float* S_last,
+                 float* ws, ssm::Launcher& launch) {
+    switch (d->k_dim) {
+        case 16: return run<TT, 16>(d, q, k, v, g, b, w, S0, scale, o, S_last, ws, launch);
+        case 32: return run<TT, 32>(d, q, k, v, g, b, w, S0, scale, o, S_last, ws, launch);
+        case 64: return run<TT, 64>(d, q, k, v, g, b, w, S0, scale, o, S_last, ws, launch);
+        default: return run<TT, 128>(d, q, k, v, g, b, w, S0, scale, o, S_last, ws, launch);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_gdn2_chunked_workspace_bytes(const ssm_gdn2_dims* dims) {
+    if (check_dims(dims) != SSM_OK) return 0;
+    return ws_bytes_for(dims);
+}
+
+ssm_status ssm_gdn2_fwd_chunked(const ssm_gdn2_dims* dims, const void* q, const void* k, const void* v,
+                                const void* g, const void* b, const void* w, const float* S0, float scale,
+                                void* o, float* S_last, void* ws, size_t ws_bytes, hipStream_t stream,
+                                ssm_timing* timing) {
+    SSM_TRY(check_dims(dims));
+    if (dims->seqlen == 0)  // nothing to chunk: S_last = S0 (or zeros)
+        return ssm_gdn2_fwd(dims, q, k, v, g, b, w, S0, scale, o, S_last, stream, timing);
+    if (!q || !k || !v || !g || !b || !w || !o) return SSM_E_NULLPTR;
+    if (S_last && S_last == S0) return SSM_E_UNSUPPORTED;
+    const void* ptrs[] = {q, k, v, g, b, w, S0, o, S_last, ws};
+    for (const void* p : ptrs)
+        if (p && ssm::misaligned(p)) return SSM_E_ALIGN;
+    if (!ws || ws_bytes < ws_bytes_for(dims)) return SSM_E_WORKSPACE;
+    (void)hipGetLastError();
+    ssm::Launcher launch{stream, timing};
+    float* wsf = static_cast<float*>(ws);
+    if (dims->io_dtype == SSM_BF16)
+        return run_k<ssm::bf16_t>(dims, q, k, v, g, b, w, S0, scale, o, S_last, wsf, launch);
+    return run_k<float>(dims, q, k, v, g, b, w, S0, scale, o, S_last, wsf, launch);
+}
+
+}  // extern "C"

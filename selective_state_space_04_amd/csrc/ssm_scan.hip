@@ -1041,6 +1041,8 @@ const char* ssm_kernel_name(int32_t id) {
         case SSM_K_CONV_RING: return "k_conv_ring";
         case SSM_K_BLOCK_BC: return "k_block_bc";
         case SSM_K_GDN2_FWD: return "k_gdn2_fwd";
+        case SSM_K_GDN2_WY: return "k_gdn2_wy";
+        case SSM_K_GDN2_STATE: return "k_gdn2_state";
     }
     return "?";
 }

@@ -138,3 +138,125 @@ def test_extreme_gates():
     ro, rS = gdn2.recurrent(*[inp[n] for n in NAMES], inp["S0"], 0.25)
     for h in range(4):
         assert _rel(o[:, h], ro[:, h]) <= TOL and _rel(S[:, h], rS[:, h]) <= TOL, h
+
+
+# ------------------------------------------------------------------ chunked form
+# ssm_gdn2_fwd_chunked: the WY form in 64-token chunks on MFMA, checked against
+# the same f64 recurrence (it is the same operation regrouped), across key
+# dimensions, ragged last chunks, initial states, strongly gated heads, bf16
+# activations and the full workload.
+
+def _runc(t, scale, **kw):
+    o, S = ssm.ssm_gdn2_fwd_chunked(*[t[n] for n in NAMES], t["S0"], scale=scale, **kw)
+    torch.cuda.synchronize()
+    return o, S
+
+
+@pytest.mark.parametrize("kd", [16, 32, 64, 128])
+@pytest.mark.parametrize("shape", [(2, 3, 1, 16), (1, 2, 64, 32), (2, 1, 100, 48), (1, 2, 333, 16)])
+@pytest.mark.parametrize("state", [False, True])
+def test_chunked_parity(kd, shape, state):
+    b, h, L, vd = shape
+    inp = W.make_gdn2_inputs(b, h, L, kd, vd, seed=3 * kd + L + vd, with_state=state)
+    scale = 1.0 / math.sqrt(kd)
+    o, S = _runc(_dev(inp), scale)
+    ro, rS = gdn2.recurrent(*[inp[n] for n in NAMES], inp["S0"], scale)
+    assert _rel(o, ro) <= TOL and _rel(S, rS) <= TOL, (_rel(o, ro), _rel(S, rS))
+
+
+def test_chunked_long_sequence():
+    inp = W.make_gdn2_inputs(1, 2, 4096, 128, 32, seed=11, with_state=True)
+    o, S = _runc(_dev(inp), 0.125)
+    ro, rS = gdn2.recurrent(*[inp[n] for n in NAMES], inp["S0"], 0.125)
+    assert _rel(o, ro) <= TOL and _rel(S, rS) <= TOL, (_rel(o, ro), _rel(S, rS))
+
+
+def test_chunked_strong_gates():
+    """Per head: decays of 1 (g = 0), decays that wipe the state every token
+    (g = -200; a 64-token chunk's cumulative log-decay reaches -12800), a ramp
+    from mild to strong gating inside each chunk, erase and write gates at 0 and
+    1, unnormalised keys."""
+    inp = W.make_gdn2_inputs(1, 5, 200, 64, 32, seed=8, with_state=True)
+    g = inp["g"]
+    g[:, 0] = 0.0
+    g[:, 1] = -200.0
+    g[:, 2] = -np.linspace(0.0, 30.0, 200, dtype=np.float32)[:, None]
+    inp["b"][:, 3] = 1.0
+    inp["w"][:, 3] = 0.0
+    inp["b"][:, 4] = 0.0
+    inp["w"][:, 4] = 1.0
+    inp["k"][:, 4] *= 3.0
+    o, S = _runc(_dev(inp), 0.25)
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    ro, rS = gdn2.recurrent(*[inp[n] for n in NAMES], inp["S0"], 0.25)
+    for h in range(5):
+        assert _rel(o[:, h], ro[:, h]) <= TOL and _rel(S[:, h], rS[:, h]) <= TOL, (h, _rel(o[:, h], ro[:, h]))
+
+
+def test_chunked_bench_workload():
+    """The full 4 x 16 heads x 4096 tokens x 128 x 128 workload: two (batch, head)
+    sequences in full against the oracle, and every head against the token
+    recurrence kernel (itself within the tolerance of the oracle)."""
+    inp = W.make_gdn2_config("gdn2_b4h16t4096")
+    scale = 1.0 / math.sqrt(128)
+    t = _dev(inp)
+    o, S = _runc(t, scale)
+    for bi, hi in ((0, 0), (3, 15)):
+        sub = [inp[n][bi:bi + 1, hi:hi + 1] for n in NAMES]
+        ro, rS = gdn2.recurrent(*sub, None, scale)
+        assert _rel(o[bi:bi + 1, hi:hi + 1], ro) <= TOL and _rel(S[bi:bi + 1, hi:hi + 1], rS) <= TOL, (bi, hi)
+    o2, S2 = _run(t, scale)
+    for bi in range(4):
+        for hi in range(16):
+            a, r = o[bi, hi], o2[bi, hi]
+            assert float((a - r).abs().max()) <= 2 * TOL * float(r.abs().max()), (bi, hi)
+            a, r = S[bi, hi], S2[bi, hi]
+            assert float((a - r).abs().max()) <= 2 * TOL * float(r.abs().max()), (bi, hi)
+
+
+@pytest.mark.parametrize("split", [64, 128])
+def test_chunked_split_on_chunk_boundary_is_exact(split):
+    inp = W.make_gdn2_inputs(2, 2, 200, 64, 32, seed=5, with_state=True)
+    t = _dev(inp)
+    o, S = _runc(t, 0.3)
+    a = {n: t[n][:, :, :split].contiguous() for n in NAMES}
+    c = {n: t[n][:, :, split:].contiguous() for n in NAMES}
+    a["S0"] = t["S0"]
+    oa, Sa = _runc(a, 0.3)
+    c["S0"] = Sa
+    oc, Sc = _runc(c, 0.3)
+    assert torch.equal(torch.cat([oa, oc], dim=2), o) and torch.equal(Sc, S)
+
+
+def test_chunked_repeatable_empty_and_limits():
+    inp = W.make_gdn2_inputs(1, 4, 150, 32, 48, seed=6, with_state=True)
+    t = _dev(inp)
+    o1, S1 = _runc(t, 0.5)
+    o2, S2 = _runc(t, 0.5)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    e = {n: t[n][:, :, :0].contiguous() for n in NAMES}
+    e["S0"] = t["S0"]
+    _, Se = _runc(e, 0.5)
+    assert torch.equal(Se, t["S0"])
+    bad = W.make_gdn2_inputs(1, 1, 70, 32, 40, seed=7)  # v_dim not a multiple of 16
+    with pytest.raises(ssm.SsmError) as ex:
+        _runc(_dev(bad), 0.5)
+    assert ex.value.code == 7
+
+
+@pytest.mark.parametrize("kd", [32, 128])
+def test_chunked_bf16_activations(kd):
+    inp = W.make_gdn2_inputs(2, 3, 200, kd, 48, seed=kd, with_state=True)
+    for n in NAMES:
+        inp[n] = W.round_bf16(inp[n])
+    t = {n: torch.from_numpy(inp[n]).to(DEV).to(torch.bfloat16) for n in NAMES}
+    t["S0"] = torch.from_numpy(inp["S0"]).to(DEV)
+    o, S = _runc(t, 1.0 / math.sqrt(kd))
+    assert o.dtype == torch.bfloat16 and S.dtype == torch.float32
+    ro, rS = gdn2.recurrent(*[inp[n] for n in NAMES], inp["S0"], 1.0 / math.sqrt(kd))
+    assert _rel(S, rS) <= TOL
+    assert _rel(o, ro) <= 2 ** -8, _rel(o, ro)
+    t32 = {n: t[n].float() for n in NAMES}
+    t32["S0"] = t["S0"]
+    o32, S32 = _runc(t32, 1.0 / math.sqrt(kd))
+    assert torch.equal(S, S32) and torch.equal(o, o32.to(torch.bfloat16))
