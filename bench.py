@@ -7,8 +7,9 @@ arithmetic.  --config picks another of the five scan workloads (the tiny f32
 case, the Mamba-130M-shaped forward and forward+backward, the decode chain).
 Inputs are seeded synthetic tensors already resident in HBM.  The metric is
 elements (batch*seqlen*d_inner*d_state) per second; each timed step starts
-after 512 MiB of unrelated writes (the flushed time is `value`, the
-back-to-back time is reported beside it).
+after a read of 512 MiB of unrelated data, which leaves the caches cold and
+clean (the flushed time is `value`, the back-to-back time is reported beside
+it).
 
 Prints ONE JSON line.  Besides the contract fields it carries
   roofline      : the dominant kernel against HBM bandwidth: its algorithmic
@@ -141,25 +142,52 @@ def conv_bench(args):
     grads = {"dx": torch.empty_like(x), "dw": torch.empty_like(w), "dbias": torch.empty_like(bias),
              "dring0": None}
 
-    def step(timer=None):
+    def fwd(timer=None):
         ssm.ssm_conv1d_fwd(x, w, bias, y=y, timing=timer)
+
+    def bwd(timer=None):
         ssm.ssm_conv1d_bwd(x, w, bias, dy, out=grads, timing=timer)
 
     if args.copy_probe:
         copy_probe(dev)
+    copy_gbps = copy_bandwidth(dev)
 
     for _ in range(args.warmup):
-        step()
+        fwd()
+        bwd()
     torch.cuda.synchronize()
+    # Flushed: a cache flush before each of the two passes, outside its events,
+    # so that neither reads what the other (or the previous step) left in the
+    # caches, as in a model where other layers run between a layer's forward
+    # and its backward.
+    flush = CacheFlush(dev)
     timers = [ssm.LaunchTimer() for _ in range(args.steps)]
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(timers[i])
-    e1.record(stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    for i in range(args.steps):
+        flush()
+        ev[i][0].record()
+        fwd(timers[i])
+        ev[i][1].record()
+        flush()
+        ev[i][2].record()
+        bwd(timers[i])
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    ms_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_bwd = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    ms = ms_fwd + ms_bwd
+    # Unflushed: the same passes back to back (the backward then finds part of x
+    # in the Infinity Cache, and the next forward part of what the backward read).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_hot = e0.elapsed_time(e1) / args.steps
+    del flush
     per_kernel = {}
     for tm in timers:
         for kname, kms in tm.results():
@@ -183,12 +211,16 @@ def conv_bench(args):
         "config": {"workload": f"{name}: batch={bsz} seqlen={L} d_inner={D} d_conv={K}, {cfg['io']} "
                                f"activations, f32 weights and arithmetic, fwd+bwd",
                    "batch": bsz, "seqlen": L, "d_inner": D, "d_conv": K, "io_dtype": cfg["io"]},
+        "timing": {"ms_per_step_flushed": round(ms, 4), "ms_fwd_flushed": round(ms_fwd, 4),
+                   "ms_bwd_flushed": round(ms_bwd, 4), "ms_per_step_unflushed": round(ms_hot, 4),
+                   "flush": "512 MiB read before the forward and before the backward, outside their events"},
         "achieved_hbm_GBps": round(sum(kbytes.values()) / (ms * 1e-3) / 1e9, 1),
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kavg.items())},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dominant,
                      "kernel_ms": round(kavg[dominant], 4), "algorithmic_bytes_per_launch": kbytes[dominant],
-                     "measured_GBps": None if traffic is None else round(traffic / (kavg[dominant] * 1e-3) / 1e9, 1)},
+                     "traffic_over_algorithmic": None if traffic is None else round(traffic / kbytes[dominant], 3),
+                     "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(gbps / copy_gbps, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -688,6 +720,22 @@ def host_cpu():
     return {"cpu_model": model, "nproc": os.cpu_count(), "cores_available": avail}
 
 
+class CacheFlush:
+    """Reads 512 MiB (twice the 256 MB Infinity Cache) of unrelated data, so
+    that what a timed pass reads comes from HBM.  A read, not a write: a
+    written flush would leave the caches full of dirty lines that the timed
+    pass then pays to write back."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+        self.sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, out=self.sink)
+
+
 def copy_bandwidth(dev, nbytes=1 << 30, reps=5):
     """Read+write GB/s of a plain device copy of nbytes (best of reps): the
     attainable-bandwidth reference the HBM fraction is also reported against."""
@@ -815,14 +863,14 @@ def scan_bench(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Flushed: 512 MiB (twice the 256 MB Infinity Cache) written between steps,
-    # outside each step's events, so that every step starts from cold caches.
-    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    # Flushed: a cache flush between steps, outside each step's events, so that
+    # every step starts from cold caches.
+    flush = CacheFlush(dev)
     timers = [ssm.LaunchTimer() for _ in range(args.steps)]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        flush.fill_(float(i))
+        flush()
         ev[i][0].record()
         step(timers[i])
         ev[i][1].record()
@@ -888,7 +936,7 @@ def scan_bench(args):
                                f"{cfg['io']} activations, f32 state, {work}",
                    "batch": bsz, "seqlen": L, "d_inner": D, "d_state": N, "io_dtype": cfg["io"], "passes": work},
         "timing": {"ms_per_step_flushed": round(ms, 4), "ms_per_step_unflushed": round(ms_hot, 4),
-                   "flush": "512 MiB written between timed steps, outside each step's events"},
+                   "flush": "512 MiB read between timed steps, outside each step's events"},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "frac_of_copy": round(step_bytes / (ms * 1e-3) / 1e9 / copy_gbps, 4)},

@@ -47,8 +47,8 @@ constexpr int NWAVE = WG / 64;
 constexpr int TT = 64;   // tokens per wave
 constexpr int PF = 4;    // tokens fetched ahead
 constexpr int KMAX = 4;
-// The backward's unrolled path runs its TT tokens in groups of PF and ends with
-// exactly one group that mixes the run's last tokens and the K-1 look-ahead.
+// A run is whole groups of PF tokens (but a sequence's ragged last run), and a
+// group holds the K-1 token look-ahead and a token more.
 static_assert(TT % PF == 0 && PF >= KMAX, "token run must split into groups of PF >= KMAX");
 
 // ---------------------------------------------------------------- VEC channels
@@ -61,6 +61,27 @@ template <> struct Raw<bf16_t, 1> { typedef bf16_t type; };
 template <typename T, int VEC>
 __device__ __forceinline__ typename Raw<T, VEC>::type ld(const T* p) {
     return *reinterpret_cast<const typename Raw<T, VEC>::type*>(p);
+}
+
+// Streaming access to the token rows.  Every row of x and dy is read once (but
+// the K-1 token halo a neighbouring run re-reads) and every row of y and dx is
+// written once, so these loads and stores are non-temporal: they do not
+// displace lines that other data would reuse from the caches.
+__device__ __forceinline__ uint2 ld_stream(const uint2* p) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float ld_stream(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ bf16_t ld_stream(const bf16_t* p) { return *p; }
+template <typename T, int VEC>
+__device__ __forceinline__ typename Raw<T, VEC>::type ld_nt(const T* p) {
+    return ld_stream(reinterpret_cast<const typename Raw<T, VEC>::type*>(p));
 }
 
 __device__ __forceinline__ void unpack(float4 r, float v[4]) {
@@ -91,6 +112,21 @@ template <> __device__ __forceinline__ void st<bf16_t, 4>(bf16_t* p, const float
 template <> __device__ __forceinline__ void st<float, 1>(float* p, const float v[1]) { p[0] = v[0]; }
 template <> __device__ __forceinline__ void st<bf16_t, 1>(bf16_t* p, const float v[1]) {
     p[0] = from_f<bf16_t>(v[0]);
+}
+
+// non-temporal stores of one lane's VEC channels (see ld_nt)
+template <typename T, int VEC> __device__ __forceinline__ void st_nt(T* p, const float v[VEC]) {
+    if constexpr (VEC == 4 && std::is_same<T, bf16_t>::value) {
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(p));
+    } else if constexpr (VEC == 4) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 r = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
+    } else {
+        st<T, VEC>(p, v);
+    }
 }
 
 // sigmoid(p) = 1 / (1 + exp(-p)) with the hardware exp2 and reciprocal.  No sign
@@ -157,7 +193,7 @@ __device__ __forceinline__ void fwd_token(const float wk[VEC][K], const float bs
         const float pre = conv_pre<K>(bs[v], wk[v], tap);
         out[v] = pre * sigmoid_c(pre);
     }
-    st<T, VEC>(yrow, out);
+    st_nt<T, VEC>(yrow, out);
 }
 
 template <typename T, int K, int VEC>
@@ -180,12 +216,13 @@ __global__ __launch_bounds__(WG) void k_conv_fwd(const T* __restrict__ x, const 
     for (int j = 0; j < K - 1; ++j) input_at<T, K, VEC>(x, ring0, b, c0, t0 - (K - 1) + j, L, D, win[j]);
     const T* xp = x + (int64_t)b * L * D + c0;
     T* yp = y + (int64_t)b * L * D + c0;
-    if (t1 - t0 == TT) {
-        // whole run inside the sequence: PF tokens in flight, no range tests in
-        // the body, so the window rotates through registers without copies
+    const int tf = t0 + (t1 - t0) / PF * PF;  // end of the run's whole groups of PF tokens
+    if (tf > t0) {
+        // whole groups: PF tokens in flight, no range tests in the body, so the
+        // window rotates through registers without copies
         R q[PF];
 #pragma unroll
-        for (int p = 0; p < PF; ++p) q[p] = ld<T, VEC>(xp + (int64_t)(t0 + p) * D);
+        for (int p = 0; p < PF; ++p) q[p] = ld_nt<T, VEC>(xp + (int64_t)(t0 + p) * D);
         // Every group of PF tokens but the last fetches the PF tokens after it, all
         // inside the run: with no per-token fetch test the queue is refilled in
         // place, so no wait on the loads just issued is needed at the loop's end.
@@ -193,20 +230,19 @@ __global__ __launch_bounds__(WG) void k_conv_fwd(const T* __restrict__ x, const 
 #pragma unroll
             for (int p = 0; p < PF; ++p) {
                 unpack(q[p], win[K - 1]);
-                if constexpr (decltype(fetch)::value) q[p] = ld<T, VEC>(xp + (int64_t)(u + p + PF) * D);
+                if constexpr (decltype(fetch)::value) q[p] = ld_nt<T, VEC>(xp + (int64_t)(u + p + PF) * D);
                 fwd_token<T, K, VEC>(wk, bs, win, yp + (int64_t)(u + p) * D);
                 shift_window<K, VEC>(win);
             }
         };
         int u = t0;
-        for (; u + PF < t1; u += PF) group(u, std::true_type{});
+        for (; u + PF < tf; u += PF) group(u, std::true_type{});
         group(u, std::false_type{});
-    } else {
-        for (int u = t0; u < t1; ++u) {
-            unpack(ld<T, VEC>(xp + (int64_t)u * D), win[K - 1]);
-            fwd_token<T, K, VEC>(wk, bs, win, yp + (int64_t)u * D);
-            shift_window<K, VEC>(win);
-        }
+    }
+    for (int u = tf; u < t1; ++u) {  // a ragged last run's remaining tokens
+        unpack(ld<T, VEC>(xp + (int64_t)u * D), win[K - 1]);
+        fwd_token<T, K, VEC>(wk, bs, win, yp + (int64_t)u * D);
+        shift_window<K, VEC>(win);
     }
     // the last K-1 inputs (oldest first) continue the stream
     if (t1 == L && ring_last) {
@@ -269,11 +305,11 @@ __device__ __forceinline__ void bwd_step(const float wk[VEC][K], const float bs[
             for (int k = 0; k < K; ++k) acc = __builtin_fmaf(wk[v][k], gw[K - 1 - k][v], acc);
             o[v] = acc;
         }
-        st<T, VEC>(dxrow, o);
+        st_nt<T, VEC>(dxrow, o);
     }
 }
 
-// part: [Bt * gridDim.y, D, K+1] per-workgroup sums (dw taps, then dbias).
+// part: [Bt * gridDim.y, K+1, D] per-workgroup sums (dw taps, then dbias).
 template <typename T, int K, int VEC>
 __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const float* __restrict__ w,
                                                  const float* __restrict__ bias,
@@ -309,8 +345,6 @@ __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const 
         const T* xp = x + base;
         const T* gp = dy + base;
         T* dxp = dx + base;
-        // a run whose K-1 token look-ahead also lies inside the sequence takes the
-        // unrolled path below after its first K-1 tokens
         // ring entry j (input time j-(K-1)) feeds tokens 0..j through tap j-t; it
         // is final once gw[t+1] = g[t] for t = 0 .. K-2 (after token K-2 entered)
         auto ring_grad = [&]() {
@@ -325,23 +359,29 @@ __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const 
                 }
         };
         const int uend = t1 + K - 1;  // tokens entering: the run plus the look-ahead
-        if (t1 - t0 == TT && t1 + K - 1 <= L) {
-            // The run and its K-1 token look-ahead lie inside the sequence.  The
-            // first K-1 tokens (no dx yet) and the first PF of the rest are fetched
-            // together; the rest stream with PF tokens in flight and no range test
-            // in the bodies, so both windows rotate through registers.
+        if (t1 - t0 >= PF) {
+            // The first K-1 tokens (no dx yet) and the first PF of the rest are
+            // fetched together; the rest stream with PF tokens in flight.  Groups
+            // of own tokens need no range test; the last group or two hold the
+            // run's last tokens and the K-1 token look-ahead (zero past the
+            // sequence end, and a ragged last run is padded to whole groups), with
+            // wave-uniform tests only.  Both windows rotate through registers.
             const int ugen = t0 + K - 1;
-            const int ulast = uend - 1;
+            const int ulim = min(uend, L);  // entering tokens that exist
             R hx[K > 1 ? K - 1 : 1], hg[K > 1 ? K - 1 : 1], qx[PF], qg[PF];
 #pragma unroll
             for (int i = 0; i < K - 1; ++i) {
-                hx[i] = ld<T, VEC>(xp + (int64_t)(t0 + i) * D);
-                hg[i] = ld<T, VEC>(gp + (int64_t)(t0 + i) * D);
+                hx[i] = ld_nt<T, VEC>(xp + (int64_t)(t0 + i) * D);
+                hg[i] = ld_nt<T, VEC>(gp + (int64_t)(t0 + i) * D);
             }
 #pragma unroll
             for (int p = 0; p < PF; ++p) {
-                qx[p] = ld<T, VEC>(xp + (int64_t)(ugen + p) * D);
-                qg[p] = ld<T, VEC>(gp + (int64_t)(ugen + p) * D);
+                if (ugen + p < ulim) {
+                    qx[p] = ld_nt<T, VEC>(xp + (int64_t)(ugen + p) * D);
+                    qg[p] = ld_nt<T, VEC>(gp + (int64_t)(ugen + p) * D);
+                } else {
+                    qx[p] = qg[p] = R{};
+                }
             }
 #pragma unroll
             for (int i = 0; i < K - 1; ++i) {
@@ -359,22 +399,26 @@ __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const 
                     float xn[VEC], dyn[VEC];
                     unpack(qx[p], xn);
                     unpack(qg[p], dyn);
-                    if (u + PF <= ulast) {
-                        qx[p] = ld<T, VEC>(xp + (int64_t)(u + PF) * D);
-                        qg[p] = ld<T, VEC>(gp + (int64_t)(u + PF) * D);
+                    if (u + PF < ulim) {
+                        qx[p] = ld_nt<T, VEC>(xp + (int64_t)(u + PF) * D);
+                        qg[p] = ld_nt<T, VEC>(gp + (int64_t)(u + PF) * D);
                     }
                     bwd_step<T, K, VEC>(wk, bs, xw, gw, true, true, true, xn, dyn, dwa, dba,
                                         dxp + (int64_t)(u - (K - 1)) * D);
                 }
             }
-            if (u0 < uend) {  // the last own tokens and the look-ahead: exactly PF steps
+            for (; u0 < uend; u0 += PF) {  // the run's last tokens and the look-ahead
 #pragma unroll
                 for (int p = 0; p < PF; ++p) {
                     const int u = u0 + p;
                     float xn[VEC], dyn[VEC];
                     unpack(qx[p], xn);
                     unpack(qg[p], dyn);
-                    bwd_step<T, K, VEC>(wk, bs, xw, gw, true, u < t1, true, xn, dyn, dwa, dba,
+                    if (u + PF < ulim) {
+                        qx[p] = ld_nt<T, VEC>(xp + (int64_t)(u + PF) * D);
+                        qg[p] = ld_nt<T, VEC>(gp + (int64_t)(u + PF) * D);
+                    }
+                    bwd_step<T, K, VEC>(wk, bs, xw, gw, u < L, u < t1, u < uend, xn, dyn, dwa, dba,
                                         dxp + (int64_t)(u - (K - 1)) * D);
                 }
             }
@@ -383,8 +427,8 @@ __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const 
                 const bool have = u < L;
                 float xn[VEC], dyn[VEC];
                 if (have) {
-                    unpack(ld<T, VEC>(xp + (int64_t)u * D), xn);
-                    unpack(ld<T, VEC>(gp + (int64_t)u * D), dyn);
+                    unpack(ld_nt<T, VEC>(xp + (int64_t)u * D), xn);
+                    unpack(ld_nt<T, VEC>(gp + (int64_t)u * D), dyn);
                 } else {
 #pragma unroll
                     for (int v = 0; v < VEC; ++v) xn[v] = dyn[v] = 0.0f;
@@ -404,11 +448,19 @@ __global__ __launch_bounds__(WG) void k_conv_bwd(const T* __restrict__ x, const 
         red[wave][K * VEC + v][lane] = dba[v];
     }
     __syncthreads();
-    for (int e = wave; e < NP; e += NWAVE) {
-        const float s = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
-        const int k = e / VEC, v = e % VEC;
-        if (c0 + v < D)
-            part[(((int64_t)b * gridDim.y + blockIdx.y) * D + c0 + v) * (K + 1) + k] = s;
+    // row k of this workgroup's partials (dw tap k, or dbias at k = K) holds the
+    // D channels contiguously, so each lane stores its VEC channels in one piece
+    if (c0 < D) {
+        float* prow = part + ((int64_t)b * gridDim.y + blockIdx.y) * (K + 1) * D + c0;
+        for (int k = wave; k <= K; k += NWAVE) {
+            float s[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const int e = k * VEC + v;
+                s[v] = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
+            }
+            st<float, VEC>(prow + (int64_t)k * D, s);
+        }
     }
 }
 
@@ -440,7 +492,7 @@ __global__ __launch_bounds__(WG) void k_conv_bwd_reduce(const float* __restrict_
     __syncthreads();
     if (wave == 0 && idx < per) {
         const float tot = ((q[0][lane] + q[1][lane]) + q[2][lane]) + q[3][lane];
-        const int d = (int)(idx / (K + 1)), k = (int)(idx % (K + 1));
+        const int k = (int)(idx / D), d = (int)(idx % D);
         if (k < K) dw[(int64_t)d * K + k] = tot;
         else dbias[d] = tot;
     }
@@ -510,6 +562,7 @@ ConvPlan conv_plan(const ssm_conv_dims* d) {
 size_t conv_ws_bytes(const ConvPlan& p) {
     return sizeof(float) * (size_t)(p.Bt * p.gy * p.D * (p.K + 1));
 }
+
 
 struct Launcher {
     ssm::Launcher l;
