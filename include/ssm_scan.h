@@ -82,14 +82,16 @@ typedef struct {
     int32_t io_dtype; /* ssm_dtype */
 } ssm_dims;
 
-#define SSM_TIMING_MAX 16
+#define SSM_TIMING_MAX 64
 
 /* Optional launch log.  When a non-NULL ssm_timing* is passed, the library
- * records events[2*i] before and events[2*i+1] after its i-th kernel launch on
- * `stream` (for i < capacity <= SSM_TIMING_MAX) and writes the kernel's id
- * into kernel_id[i]; `count` is incremented per recorded launch (the caller
- * zeroes it).  The caller creates the events (hipEventCreate) and reads them
- * after synchronising.  Used for per-kernel timing; NULL costs nothing. */
+ * records events[2*i] before and events[2*i+1] after its i-th kernel launch
+ * (ssm_block.h: also each hipBLASLt GEMM) on `stream` (for i < capacity <=
+ * SSM_TIMING_MAX) and writes the kernel's id into kernel_id[i]; `count` is
+ * incremented per recorded launch (the caller zeroes it); launches past the
+ * capacity are not recorded.  The caller creates the events (hipEventCreate)
+ * and reads them after synchronising.  Used for per-kernel timing; NULL costs
+ * nothing. */
 typedef struct {
     hipEvent_t *events;
     int32_t capacity;
@@ -117,7 +119,9 @@ enum {
     SSM_K_BLOCK_BC = 16,     /* x_proj's B/C columns split / joined (ssm_block.h) */
     SSM_K_GDN2_FWD = 17,     /* Gated DeltaNet-2 forward recurrence (ssm_gdn2.h) */
     SSM_K_GDN2_WY = 18,      /* GDN2 chunked form: key side per chunk (decays, A, P, M^-1) */
-    SSM_K_GDN2_STATE = 19    /* GDN2 chunked form: state pass over the chunks (MFMA) */
+    SSM_K_GDN2_STATE = 19,   /* GDN2 chunked form: state pass over the chunks (MFMA) */
+    SSM_K_BLOCK_GEMM = 20,   /* one projection GEMM of the block (hipBLASLt; ssm_block.h) */
+    SSM_K_BLOCK_SUM = 21     /* fixed-order sum of a split weight gradient's partials */
 };
 
 /* Name of a kernel id (for matching profiler output); "?" if unknown. */

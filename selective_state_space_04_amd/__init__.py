@@ -27,7 +27,7 @@ LIB_PATH = os.environ.get("SSM_SCAN_LIB") or os.path.join(_HERE, "libssmscan.so"
 
 SSM_F32, SSM_BF16 = 0, 1
 D_STATE = 16
-TIMING_MAX = 16
+TIMING_MAX = 64
 
 
 class SsmDims(ctypes.Structure):

@@ -260,11 +260,14 @@ const LtPlan* get_plan(ssm_block_ctx* ctx, bool ta, bool tb, int64_t m, int64_t 
     return &ctx->plans.back();
 }
 
+// The projections' GEMMs: the caller's stream, GEMM_WS bytes of workspace and
+// the caller's optional launch log (each GEMM is logged as SSM_K_BLOCK_GEMM).
 struct Gemm {
     ssm_block_ctx* ctx;
     hipDataType ab, io_c;
     hipStream_t s;
     void* ws;  // GEMM_WS bytes
+    ssm_timing* tm;
     ssm_status operator()(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
                           const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
                           bool f32_out = false, int32_t batch = 1, int64_t sA = 0, int64_t sB = 0,
@@ -273,8 +276,15 @@ struct Gemm {
         const LtPlan* e = get_plan(ctx, ta, tb, m, n, k, lda, ldb, ldc, ab, f32_out ? HIP_R_32F : io_c, batch,
                                    sA, sB, sC);
         if (!e) return SSM_E_UNSUPPORTED;
+        const bool rec = tm && tm->events && tm->count < tm->capacity && tm->count < SSM_TIMING_MAX;
+        if (rec) (void)hipEventRecord(tm->events[2 * tm->count], s);
         const hipblasStatus_t st = hipblasLtMatmul(ctx->lt, e->op, &alpha, B, e->a, A, e->b, &beta, C, e->c, C,
                                                    e->c, &e->algo, e->ws ? ws : nullptr, e->ws, s);
+        if (rec) {
+            (void)hipEventRecord(tm->events[2 * tm->count + 1], s);
+            tm->kernel_id[tm->count] = SSM_K_BLOCK_GEMM;
+            tm->count++;
+        }
         return st == HIPBLAS_STATUS_SUCCESS ? SSM_OK : SSM_E_LAUNCH;
     }
 };
@@ -292,14 +302,15 @@ __global__ __launch_bounds__(WG) void k_sum_parts(const float* __restrict__ part
 // Row-major f32 weight gradient C[m, n] = A^T B over T tokens, A [T, m] (lda),
 // B [T, n] (ldb), with the tokens split as described at wgrad_splits.
 ssm_status wgrad(const Gemm& g, int64_t m, int64_t n, int64_t T, const void* A, int64_t lda, const void* B,
-                 int64_t ldb, float* C, float* part, ssm_timing* tm) {
+                 int64_t ldb, float* C, float* part) {
+    ssm_timing* tm = g.tm;
     const int64_t S = wgrad_splits(m, n, T);
     if (S == 1) return g(true, false, m, n, T, A, lda, B, ldb, 0.0f, C, n, true);
     const int64_t Tc = T / S;
     SSM_TRY(g(true, false, m, n, Tc, A, lda, B, ldb, 0.0f, part, n, true, (int32_t)S, Tc * lda, Tc * ldb, m * n));
     ssm::Launcher launch{g.s, tm};
     const int64_t mn = m * n;
-    return launch(SSM_K_BLOCK_BC, k_sum_parts, dim3((unsigned)((mn + WG - 1) / WG)), dim3(WG),
+    return launch(SSM_K_BLOCK_SUM, k_sum_parts, dim3((unsigned)((mn + WG - 1) / WG)), dim3(WG),
                   (const float*)part, C, mn, (int)S);
 }
 
@@ -422,7 +433,7 @@ ssm_status ssm_block_fwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
          *Bm = act + s.Bm, *Cm = act + s.Cm, *dt = act + s.dt, *ys = act + s.ys;
     float* ckpt = saved ? reinterpret_cast<float*>(act + s.ckpt) : nullptr;
     const hipDataType io_t = q.io == SSM_BF16 ? HIP_R_16BF : HIP_R_32F;
-    const Gemm gemm{ctx, io_t, io_t, stream, static_cast<char*>(ws) + w.gemm};
+    const Gemm gemm{ctx, io_t, io_t, stream, static_cast<char*>(ws) + w.gemm, timing};
     const char* W_in = static_cast<const char*>(p->W_in);
     const size_t half = (size_t)q.di * q.dm * q.esz;
     SSM_TRY(gemm(false, true, q.T, q.di, q.dm, X, q.dm, W_in, q.dm, 0.0f, xi, q.di));
@@ -467,11 +478,11 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     void *dys = wb + w.dys, *dxc = wb + w.dxc, *ddt = wb + w.ddt, *ddtl = wb + w.ddtl, *dB = wb + w.dB,
          *dC = wb + w.dC, *dz = wb + w.dz, *dproj = wb + w.dproj, *dxi = wb + w.dxi;
     const hipDataType io_t = q.io == SSM_BF16 ? HIP_R_16BF : HIP_R_32F;
-    const Gemm gemm{ctx, io_t, io_t, stream, wb + w.gemm};
+    const Gemm gemm{ctx, io_t, io_t, stream, wb + w.gemm, timing};
     // out_proj
     SSM_TRY(gemm(false, false, q.T, q.di, q.dm, dY, q.dm, p->W_out, q.di, 0.0f, dys, q.di));
     float* part = reinterpret_cast<float*>(wb + w.part);
-    SSM_TRY(wgrad(gemm, q.dm, q.di, q.T, dY, q.dm, ys, q.di, g->dW_out, part, timing));
+    SSM_TRY(wgrad(gemm, q.dm, q.di, q.T, dY, q.dm, ys, q.di, g->dW_out, part));
     // scan
     const ssm_dims sd = scan_dims(q);
     SSM_TRY(ssm_scan_bwd(&sd, xc, dt, Bm, Cm, z, p->A_log, p->D, p->dt_bias, nullptr, ckpt, dys, dxc, ddt, dB,
@@ -479,11 +490,11 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
                          timing));
     // dt_proj, then x_proj's gradient rows [d dt_low | dB | dC]
     SSM_TRY(gemm(false, false, q.T, q.R, q.di, ddt, q.di, p->W_dt, q.R, 0.0f, ddtl, q.R));
-    SSM_TRY(wgrad(gemm, q.di, q.R, q.T, ddt, q.di, dtl, q.R, g->dW_dt, part, timing));
+    SSM_TRY(wgrad(gemm, q.di, q.R, q.T, ddt, q.di, dtl, q.R, g->dW_dt, part));
     SSM_TRY(launch_proj(q, false, ddtl, dB, dC, dproj, stream, timing));
     // x_proj: dxc += dproj W_x
     SSM_TRY(gemm(false, false, q.T, q.di, q.P, dproj, q.P, p->W_x, q.di, 1.0f, dxc, q.di));
-    SSM_TRY(wgrad(gemm, q.P, q.di, q.T, dproj, q.P, xc, q.di, g->dW_x, part, timing));
+    SSM_TRY(wgrad(gemm, q.P, q.di, q.T, dproj, q.P, xc, q.di, g->dW_x, part));
     // conv1d + SiLU
     const ssm_conv_dims cd = conv_dims(q);
     SSM_TRY(ssm_conv1d_bwd(&cd, xi, p->conv_w, p->conv_b, nullptr, dxc, dxi, g->dconv_w, g->dconv_b, nullptr,
@@ -493,8 +504,8 @@ ssm_status ssm_block_bwd(ssm_block_ctx* ctx, const ssm_block_dims* dims, const v
     const size_t half = (size_t)q.di * q.dm * q.esz;
     SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dxi, q.di, W_in, q.dm, 0.0f, dX, q.dm));
     SSM_TRY(gemm(false, false, q.T, q.dm, q.di, dz, q.di, W_in + half, q.dm, 1.0f, dX, q.dm));
-    SSM_TRY(wgrad(gemm, q.di, q.dm, q.T, dxi, q.di, X, q.dm, g->dW_in, part, timing));
-    return wgrad(gemm, q.di, q.dm, q.T, dz, q.di, X, q.dm, g->dW_in + (size_t)q.di * q.dm, part, timing);
+    SSM_TRY(wgrad(gemm, q.di, q.dm, q.T, dxi, q.di, X, q.dm, g->dW_in, part));
+    return wgrad(gemm, q.di, q.dm, q.T, dz, q.di, X, q.dm, g->dW_in + (size_t)q.di * q.dm, part);
 }
 
 }  // extern "C"

@@ -1043,6 +1043,8 @@ const char* ssm_kernel_name(int32_t id) {
         case SSM_K_GDN2_FWD: return "k_gdn2_fwd";
         case SSM_K_GDN2_WY: return "k_gdn2_wy";
         case SSM_K_GDN2_STATE: return "k_gdn2_state";
+        case SSM_K_BLOCK_GEMM: return "block_gemm";
+        case SSM_K_BLOCK_SUM: return "k_sum_parts";
     }
     return "?";
 }

@@ -5,11 +5,12 @@ around the HIP conv1d + SiLU and selective scan) against the f64 block oracle
 Pass criterion per tensor: max |gpu - oracle| <= rtol * max |oracle|, with
   rtol = 1e-4 for f32 (the scan's own f32 gradient bound; f32 GEMM sums add
          ~1e-6 relative), and
-  rtol = 5e-2 for bf16 activations and projection weights: every stored bf16
+  rtol = 2e-2 for bf16 activations and projection weights: every stored bf16
          activation adds up to 2^-9 relative rounding, and the forward chain
          in_proj -> conv -> x_proj -> dt_proj -> scan -> out_proj stores six of
-         them in sequence (about 1.5% expected), the backward chain about ten
-         (about 3%).
+         them in sequence, the backward chain about ten: 10 x 2^-9 = 1.95% if
+         every rounding erred the same way, about sqrt(10) x 2^-9 = 0.6% for
+         independent roundings (measured: 0.3-1%).
 At the full Mamba-2.8B layer size the oracle runs on a prefix: the block is
 causal and batch rows are independent, so the first tokens of row 0 depend only
 on themselves, and with dY zero outside that prefix every gradient (dX and all
@@ -27,7 +28,7 @@ ssm = pytest.importorskip("selective_state_space_04_amd")
 pytestmark = pytest.mark.gpu
 
 F32_TOL = 1e-4
-BF16_TOL = 5e-2
+BF16_TOL = 2e-2
 DEV = torch.device("cuda:0")
 IO_PARAMS = ("W_in", "W_x", "W_dt", "W_out")
 
@@ -129,6 +130,31 @@ def test_block_backward_is_deterministic(ctx):
     torch.cuda.synchronize()
     for n in g1:
         assert torch.equal(g1[n], g2[n]), n
+
+
+def test_block_on_a_non_default_stream(ctx):
+    """A block forward and backward on a non-default stream give the same bits as
+    on the default stream, and work that stream receives after the call (zeroing
+    every output) runs after all of the call's work."""
+    X, p, dY = W.make_block_inputs(2, 700, 64, 128, 16, 8, 4, seed=58, bf16=True)
+    Xd, pd, dYd = _dev(X, p, dY, torch.bfloat16)
+    Y, saved = ssm.ssm_block_fwd(ctx, Xd, pd)
+    g_ref = ssm.ssm_block_bwd(ctx, Xd, pd, saved, dYd)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        Y2, saved2 = ssm.ssm_block_fwd(ctx, Xd, pd, stream=s)
+        g = ssm.ssm_block_bwd(ctx, Xd, pd, saved2, dYd, stream=s)
+        kept = {n: t.clone() for n, t in g.items()}
+        kept["Y"] = Y2.clone()
+        for t in g.values():
+            t.zero_()
+    torch.cuda.synchronize()
+    assert torch.equal(kept["Y"], Y)
+    for n, t in g.items():
+        assert torch.count_nonzero(t) == 0, n
+        assert torch.equal(kept[n], g_ref[n]), n
 
 
 def test_block_inference_forward_matches_training_forward(ctx):
