@@ -39,7 +39,6 @@ namespace {
 
 constexpr int CH = 64;       // tokens per chunk
 constexpr int WGK = 256;     // threads of the key-side kernel
-constexpr int NBLK = 136;    // 4x4 blocks of the lower triangle of a CH x CH matrix
 constexpr int XCDS = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -68,49 +67,115 @@ __host__ __device__ constexpr int aop(int tile, int m, int lane, int nb) {
     return ((tile * (nb / 4) + m / 4) * 64 + lane) * 4 + m % 4;
 }
 
+__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Key side of one chunk.  grid (chunks, pairs), WGK threads.
+//
+// A and P by 16-token blocks.  For a block pair bi > bj both factors of
+//   exp(G_i - G_j) = exp(G_i - E_bj) * exp(E_bj - G_j),
+// E_bj = G at block bj's last token, have exponent <= 0 (G falls along the
+// chunk), so the block is a product of two decayed operands on MFMA with no
+// overflow for any gate strength: the six block pairs give twelve 16 x 16
+// products (A and P), three per wave.  The four diagonal blocks keep the
+// per-element exponential (136 entries each, j <= i, spread over all threads).
 template <typename TT, int K>
 __global__ __launch_bounds__(WGK) void k_gdn2_wy(const TT* __restrict__ q, const TT* __restrict__ k,
                                                  const TT* __restrict__ g, const TT* __restrict__ b,
                                                  float* __restrict__ ws, int T, int nch) {
     constexpr int KC = K < 32 ? K : 32;  // key dimensions staged per pass
+    constexpr int RP = CH + 4;           // padded staging row: MFMA operand reads hit 64 banks
+    constexpr int NDIAG = 4 * 136;       // entries j <= i of the four diagonal 16 x 16 blocks
+    constexpr int DPT = (NDIAG + WGK - 1) / WGK;
     using L = Lay<K>;
-    __shared__ float Gs[KC][CH], ks[KC][CH], bks[KC][CH], qs[KC][CH];
-    __shared__ float As[CH][CH], Ps[CH][CH], Ms[CH][CH];
+    // staging for the passes (g, k, b*k, q as [key][token]); after them the same
+    // memory holds A, P and M^-1
+    __shared__ float lds[3 * CH * CH];
+    float(*As)[CH] = reinterpret_cast<float(*)[CH]>(lds);
+    float(*Ps)[CH] = reinterpret_cast<float(*)[CH]>(lds + CH * CH);
+    float(*Ms)[CH] = reinterpret_cast<float(*)[CH]>(lds + 2 * CH * CH);
+    static_assert(4 * KC * RP <= 3 * CH * CH, "staging must fit the A/P/M^-1 region");
+    static_assert(CH * KC % WGK == 0, "whole staged elements per thread");
     const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = blockIdx.x;
     const int64_t pair = blockIdx.y;
     const int t0 = c * CH;
     const int n = min(CH, T - t0);
     float* out = ws + (pair * nch + c) * (int64_t)L::total;
     const int64_t row0 = pair * T + t0;
-    for (int e = tid; e < CH * CH; e += WGK) {
-        (&As[0][0])[e] = 0.0f;
-        (&Ps[0][0])[e] = 0.0f;
-    }
-    // this thread's 4x4 block (bi, bj), bj <= bi, of A and P
-    int bi = 0, bj = tid;
-    while (bj > bi) {
-        bj -= bi + 1;
-        ++bi;
-    }
-    const bool blk = tid < NBLK;
-    float Aa[4][4], Pa[4][4];
+    // this wave's three off-diagonal products: chain h = 3 wv + s over the list
+    // (bi, bj) = (1,0) (2,0) (3,0) (2,1) (3,1) (3,2), A then P for each pair
+    int cbi[3], cbj[3];
+    bool cisP[3];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int s3 = 0; s3 < 3; ++s3) {
+        const int h = 3 * wv + s3, pr = h >> 1;
+        cbi[s3] = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
+        cbj[s3] = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
+        cisP[s3] = h & 1;
+    }
+    f4 acc[3];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) Aa[a][cc] = Pa[a][cc] = 0.0f;
-    for (int kc = 0; kc < K / KC; ++kc) {
-        for (int e = tid; e < CH * KC; e += WGK) {
+    for (int s3 = 0; s3 < 3; ++s3) acc[s3] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    // this thread's diagonal entries (block db, row il, column jl <= il)
+    int dI[DPT], dJ[DPT];
+    float dA[DPT], dP[DPT];
+#pragma unroll
+    for (int r = 0; r < DPT; ++r) {
+        const int e = tid + r * WGK;
+        const int ee = e < NDIAG ? e : 0;
+        const int db = ee / 136;
+        int il = 0, jl = ee % 136;
+        while (jl > il) {
+            jl -= il + 1;
+            ++il;
+        }
+        dI[r] = 16 * db + il;
+        dJ[r] = e < NDIAG ? 16 * db + jl : -1;  // -1: no entry
+        dA[r] = dP[r] = 0.0f;
+    }
+    const int i16 = l & 15, kq = l >> 4;  // MFMA operand: row/column i16, key kq of each 4-key step
+    // each pass's inputs are fetched into registers during the previous pass
+    constexpr int EPT = CH * KC / WGK;  // staged elements per thread and pass
+    float pk[EPT], pb[EPT], pq[EPT], pg[EPT];
+    auto fetch = [&](int kc) {
+#pragma unroll
+        for (int r = 0; r < EPT; ++r) {
+            const int e = tid + r * WGK;
             const int tok = e / KC, kl = e % KC;
             const bool valid = tok < n;
-            const int64_t src = (row0 + tok) * K + kc * KC + kl;
-            const float kv = valid ? ld(k, src) : 0.0f;
-            ks[kl][tok] = kv;
-            bks[kl][tok] = valid ? ld(b, src) * kv : 0.0f;
-            qs[kl][tok] = valid ? ld(q, src) : 0.0f;
-            Gs[kl][tok] = valid ? ld(g, src) : 0.0f;  // a padded token is the identity: g = 0
+            const int64_t src = (row0 + min(tok, n - 1)) * K + kc * KC + kl;
+            pk[r] = valid ? ld(k, src) : 0.0f;
+            pb[r] = valid ? ld(b, src) : 0.0f;
+            pq[r] = valid ? ld(q, src) : 0.0f;
+            pg[r] = valid ? ld(g, src) : 0.0f;  // a padded token is the identity: g = 0
         }
+    };
+    fetch(0);
+#pragma unroll 1
+    for (int kc = 0; kc < K / KC; ++kc) {
+        // The staging addresses are the same in every pass; hoisted out of the
+        // loop they would hold about 110 more registers for its whole length (one
+        // wave per SIMD instead of three).  An opaque zero offset keeps them here.
+        int zz = 0;
+        asm volatile("" : "+v"(zz));
+        float(*Gs)[RP] = reinterpret_cast<float(*)[RP]>(lds + zz);
+        float(*ks)[RP] = reinterpret_cast<float(*)[RP]>(lds + zz + KC * RP);
+        float(*bks)[RP] = reinterpret_cast<float(*)[RP]>(lds + zz + 2 * KC * RP);
+        float(*qs)[RP] = reinterpret_cast<float(*)[RP]>(lds + zz + 3 * KC * RP);
+#pragma unroll
+        for (int r = 0; r < EPT; ++r) {
+            const int e = tid + r * WGK;
+            const int tok = e / KC, kl = e % KC;
+            ks[kl][tok] = pk[r];
+            bks[kl][tok] = pb[r] * pk[r];
+            qs[kl][tok] = pq[r];
+            Gs[kl][tok] = pg[r];
+        }
+        if (kc + 1 < K / KC) fetch(kc + 1);
         __syncthreads();
         if (tid < KC) {  // inclusive cumulative sum over the chunk's tokens (in registers)
             float gv[CH];
@@ -122,25 +187,34 @@ __global__ __launch_bounds__(WGK) void k_gdn2_wy(const TT* __restrict__ q, const
             for (int tok = 0; tok < CH; ++tok) Gs[tid][tok] = gv[tok];
         }
         __syncthreads();
-        if (blk) {
-            for (int kl = 0; kl < KC; ++kl) {
-                const f4 gi = *reinterpret_cast<const f4*>(&Gs[kl][4 * bi]);
-                const f4 gj = *reinterpret_cast<const f4*>(&Gs[kl][4 * bj]);
-                const f4 kj = *reinterpret_cast<const f4*>(&ks[kl][4 * bj]);
-                const f4 bki = *reinterpret_cast<const f4*>(&bks[kl][4 * bi]);
-                const f4 qi = *reinterpret_cast<const f4*>(&qs[kl][4 * bi]);
+        // off-diagonal blocks on MFMA
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
+        for (int st = 0; st < KC / 4; ++st) {
+            const int kl = 4 * st + kq;
 #pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) {
-                        // entries with j > i (upper part of a diagonal block) are
-                        // masked below; their exponent is zeroed so it stays finite
-                        const bool upper = bi == bj && cc > a;
-                        const float dec = __builtin_amdgcn_exp2f(upper ? 0.0f : (gi[a] - gj[cc]) * LOG2E);
-                        const float kd = kj[cc] * dec;
-                        Aa[a][cc] = __builtin_fmaf(bki[a], kd, Aa[a][cc]);
-                        Pa[a][cc] = __builtin_fmaf(qi[a], kd, Pa[a][cc]);
-                    }
+            for (int s3 = 0; s3 < 3; ++s3) {
+                const int ti = 16 * cbi[s3] + i16, tj = 16 * cbj[s3] + i16;
+                const float E = Gs[kl][16 * cbj[s3] + 15];
+                const float li = __builtin_amdgcn_exp2f((Gs[kl][ti] - E) * LOG2E);
+                const float rj = __builtin_amdgcn_exp2f((E - Gs[kl][tj]) * LOG2E);
+                const float av = (cisP[s3] ? qs[kl][ti] : bks[kl][ti]) * li;
+                acc[s3] = mfma(av, ks[kl][tj] * rj, acc[s3]);
+            }
+        }
+        // diagonal blocks, per element
+#pragma unroll
+        for (int r = 0; r < DPT; ++r) {
+            if (dJ[r] >= 0) {
+                const int i = dI[r], j = dJ[r];
+                float a = dA[r], pv = dP[r];
+                for (int kl = 0; kl < KC; ++kl) {
+                    const float dec = __builtin_amdgcn_exp2f((Gs[kl][i] - Gs[kl][j]) * LOG2E);
+                    const float kd = ks[kl][j] * dec;
+                    a = __builtin_fmaf(bks[kl][i], kd, a);
+                    pv = __builtin_fmaf(qs[kl][i], kd, pv);
+                }
+                dA[r] = a;
+                dP[r] = pv;
             }
         }
         // the chunk's operands for these KC key dimensions
@@ -161,15 +235,24 @@ __global__ __launch_bounds__(WGK) void k_gdn2_wy(const TT* __restrict__ q, const
         if (tid < KC) out[L::eGl + kc * KC + tid] = __builtin_amdgcn_exp2f(Gs[tid][CH - 1] * LOG2E);
         __syncthreads();
     }
-    if (blk) {
+    // A (strictly lower) and P (lower with the diagonal) into LDS, zero elsewhere
+    for (int e = tid; e < CH * CH; e += WGK) {
+        (&As[0][0])[e] = 0.0f;
+        (&Ps[0][0])[e] = 0.0f;
+    }
+    __syncthreads();
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+    for (int s3 = 0; s3 < 3; ++s3) {
+        float(*dst)[CH] = cisP[s3] ? Ps : As;
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const int i = 4 * bi + a, j = 4 * bj + cc;
-                As[i][j] = j < i ? Aa[a][cc] : 0.0f;
-                Ps[i][j] = j <= i ? Pa[a][cc] : 0.0f;
-            }
+        for (int r = 0; r < 4; ++r) dst[16 * cbi[s3] + 4 * kq + r][16 * cbj[s3] + i16] = acc[s3][r];
+    }
+#pragma unroll
+    for (int r = 0; r < DPT; ++r) {
+        if (dJ[r] >= 0) {
+            if (dJ[r] < dI[r]) As[dI[r]][dJ[r]] = dA[r];
+            Ps[dI[r]][dJ[r]] = dP[r];
+        }
     }
     __syncthreads();
     if (tid < CH) {
@@ -198,10 +281,6 @@ __global__ __launch_bounds__(WGK) void k_gdn2_wy(const TT* __restrict__ q, const
         const int ti = e / 1024, mj = (e / 64) % 16, ln = e % 64;
         out[L::Mi + aop(ti, mj, ln, 16)] = Ms[16 * ti + ln % 16][4 * mj + ln / 16];
     }
-}
-
-__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // Four consecutive A-operand blocks (4 m4 .. 4 m4 + 3) of a tile for this lane.
