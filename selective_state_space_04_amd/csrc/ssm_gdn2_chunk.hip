@@ -352,6 +352,21 @@ __global__ __launch_bounds__(StateSplit<K>::NW * 64) void k_gdn2_state(
                 paq[g4][ti] = opnd(b0 + L::Qe, ti, wv * (KBW / 4) + g4, l, KB);
             }
     }
+    // A chunk's outputs are stored after the next chunk's first loads have been
+    // issued: loads and stores retire in order, so a load issued after a store
+    // would also wait for that store.
+    f4 po[TPW];
+    int pt0 = -1;
+    auto store_o = [&]() {
+        if (pt0 < 0) return;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = pt0 + 16 * (wv * TPW + j) + 4 * quad + r;
+                if (tok < T) o[(pair * T + tok) * V + col] = ssm::from_f<TT>(scale * po[j][r]);
+            }
+    };
     for (int c = 0; c < nch; ++c) {
         const float* base = ws + (pair * nch + c) * (int64_t)L::total;
         const float* nbase = ws + (pair * nch + min(c + 1, nch - 1)) * (int64_t)L::total;
@@ -390,6 +405,7 @@ __global__ __launch_bounds__(StateSplit<K>::NW * 64) void k_gdn2_state(
                 X[ti][r] = (wv == 0 && tok < T) ? ld(w, e) * ld(v, e) : 0.0f;
                 oq[ti][r] = 0.0f;
             }
+        store_o();  // the previous chunk's outputs
 #pragma unroll
         for (int g4 = 0; g4 < KBW / 4; ++g4) {
 #pragma unroll
@@ -490,13 +506,10 @@ __global__ __launch_bounds__(StateSplit<K>::NW * 64) void k_gdn2_state(
         }
         wave_sync_lds();
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = t0 + 16 * (ti0 + j) + 4 * quad + r;
-                if (tok < T) o[(pair * T + tok) * V + col] = ssm::from_f<TT>(scale * oqt[j][r]);
-            }
+        for (int j = 0; j < TPW; ++j) po[j] = oqt[j];
+        pt0 = t0;
     }
+    store_o();
     if (S_last) {
 #pragma unroll
         for (int m = 0; m < KBW; ++m) S_last[(pair * K + key0 + 4 * m + quad) * V + col] = Skb[m];
