@@ -355,7 +355,7 @@ def decode_bench(args):
     }
     if not args.no_cpu_baseline:
         import oracle
-        rows = 8
+        rows = 96  # about 10 s of host work for the 1024 steps
         hs = np.zeros((rows, D, N))
         t0 = time.perf_counter()
         steps = 0
@@ -466,14 +466,19 @@ def block_bench(args):
     if not args.no_cpu_baseline:
         import oracle
         from oracle.block import block_bwd
+        # a prefix of batch row 0, doubled until one run takes at least 8 s
         Lp = 256
-        t0 = time.perf_counter()
-        block_bwd(np.ascontiguousarray(X[:1, :Lp]), p, np.ascontiguousarray(dY[:1, :Lp]))
-        sec = time.perf_counter() - t0
+        while True:
+            t0 = time.perf_counter()
+            block_bwd(np.ascontiguousarray(X[:1, :Lp]), p, np.ascontiguousarray(dY[:1, :Lp]))
+            sec = time.perf_counter() - t0
+            if sec >= 8.0 or 2 * Lp > L:
+                break
+            Lp *= 2
         line["cpu_baseline"] = {"value": Lp / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
                                 "kind": "oracle",
                                 "sample": f"batch row 0, the first {Lp} tokens of the same workload, forward "
-                                          f"and backward in f64 ({sec:.1f} s)"}
+                                          f"and backward in f64 ({sec:.1f} s)", **host_cpu()}
     ctx.close()
     out = json.dumps(line)
     print(out, flush=True)
@@ -548,14 +553,14 @@ def train_bench(args):
         xb = np.ascontiguousarray(Xc[idx])
         dY = np.ones_like(xb) * np.float32(2.0 / xb.size)
         reps, t0 = 0, time.perf_counter()
-        while reps < 50 and time.perf_counter() - t0 < 5.0:
+        while reps < 500 and time.perf_counter() - t0 < 10.0:
             block_bwd(xb, p0, dY)  # forward and backward of one step's batch in f64
             reps += 1
         sec = (time.perf_counter() - t0) / reps
         line["cpu_baseline"] = {"value": 1.0 / sec, "unit": "steps/s", "cores": oracle.num_threads(),
                                 "kind": "oracle",
                                 "sample": f"{reps} block forward+backward passes of one step's batch in f64, "
-                                          f"no optimizer ({sec * 1e3:.1f} ms each)"}
+                                          f"no optimizer ({sec * 1e3:.1f} ms each)", **host_cpu()}
     ctx.close()
     out = json.dumps(line)
     print(out, flush=True)
@@ -655,15 +660,19 @@ def gdn2_bench(args):
     if not args.no_cpu_baseline:
         import oracle
         from oracle import gdn2
-        Ls = 1024
-        sub = [inp[n][:1, :1, :Ls] for n in names]
-        t0 = time.perf_counter()
-        gdn2.recurrent(*sub, None, scale)
-        sec = time.perf_counter() - t0
-        line["cpu_baseline"] = {"value": Ls / H / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
+        # whole (batch, head) sequences one after another, until at least 10 s
+        npairs, sec = 0, 0.0
+        while npairs < 10000 and sec < 10.0:
+            bi, hi = (npairs // H) % B, npairs % H
+            sub = [inp[n][bi:bi + 1, hi:hi + 1] for n in names]
+            t0 = time.perf_counter()
+            gdn2.recurrent(*sub, None, scale)
+            sec += time.perf_counter() - t0
+            npairs += 1
+        line["cpu_baseline"] = {"value": npairs * L / H / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
                                 "kind": "oracle",
-                                "sample": f"batch 0, head 0, the first {Ls} tokens in f64 ({sec:.1f} s), scaled "
-                                          f"to all {H} heads of a token", **host_cpu()}
+                                "sample": f"{npairs} whole (batch, head) sequences of {L} tokens in f64 "
+                                          f"({sec:.1f} s), scaled to all {H} heads of a token", **host_cpu()}
     out = json.dumps(line)
     print(out, flush=True)
     if args.out:
@@ -824,8 +833,11 @@ def cpu_scan_baseline(inp, cfg, passes, budget_s=12.0):
     sec1 = run(1)
     per_row = max(sec1, 1e-6)
     if per_row * bsz <= budget_s:
-        reps = max(1, int(budget_s / (per_row * bsz) / 4))
-        sec = sum(run(bsz) for _ in range(reps))
+        # the whole workload, repeated until at least 10 s of host work
+        reps, sec = 0, 0.0
+        while reps < 100000 and sec < 10.0:
+            sec += run(bsz)
+            reps += 1
         rows, what = bsz, f"the whole workload ({bsz} rows), {reps} run(s)"
     else:
         rows = max(1, min(bsz, int(budget_s / per_row)))
