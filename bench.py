@@ -44,7 +44,9 @@ TRAFFIC = {"scan": (os.path.join(CSRC, "ssm_scan.hip"),
            "decode": (os.path.join(CSRC, "ssm_scan.hip"),
                       os.path.join(ROOT, "profiles", "c5_decode_step_traffic.txt")),
            "gdn2": (os.path.join(CSRC, "ssm_gdn2.hip"),
-                    os.path.join(ROOT, "profiles", "gdn2_b4h16t4096_traffic.txt"))}
+                    os.path.join(ROOT, "profiles", "gdn2_b4h16t4096_traffic.txt")),
+           "gdn2_chunked": (os.path.join(CSRC, "ssm_gdn2_chunk.hip"),
+                            os.path.join(ROOT, "profiles", "gdn2_chunked_b4h16t4096_traffic.txt"))}
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -631,9 +633,12 @@ def gdn2_bench(args):
         flops = 2048.0 * mfmas
         tflops = flops / (kavg[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(dom, "gdn2_chunked"), "kernel": dom,
                 "kernel_ms": round(kavg[dom], 4), "flops_per_launch": flops,
-                "note": "f32 MFMA (v_mfma_f32_16x16x4f32) work of the state pass as issued"}
+                "key_side_traffic": measured_traffic("k_gdn2_wy", "gdn2_chunked"),
+                "note": "f32 MFMA (v_mfma_f32_16x16x4f32) work of the state pass as issued; traffic = "
+                        "counted HBM bytes per launch of the state pass (key side beside it)"}
         form = "chunked WY form, 64-token chunks, products on MFMA"
     else:
         dom = "k_gdn2_fwd"
