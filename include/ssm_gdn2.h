@@ -59,8 +59,10 @@ ssm_status ssm_gdn2_fwd(const ssm_gdn2_dims *dims, const void *q, const void *k,
  *     P[i][j] = sum_k q_i k_j exp(G_i - G_j)      (j <= i)
  *     vn = M^{-1} (w*v - (b*k*exp(G)) S),  o = scale (P vn + (q*exp(G)) S)
  *     S  = diag(exp(G_last)) S + (k*exp(G_last - G))^T vn
- * Every exp(G_i - G_j) is formed per element with i >= j (<= 1 for g <= 0), so
- * strongly gated heads cannot overflow it.  Equal to ssm_gdn2_fwd up to f32
+ * Every exp(G_i - G_j) has i >= j (<= 1 for g <= 0) and is formed either per
+ * element (inside a 16-token block) or as exp(G_i - E) * exp(E - G_j) with E
+ * the G at the end of j's block (both factors <= 1), so strongly gated heads
+ * cannot overflow it.  Equal to ssm_gdn2_fwd up to f32
  * rounding (not bit for bit).  Chaining calls through S_last -> S0 reproduces
  * one call over the joined sequence bit for bit when every call but the last
  * has a multiple of 64 tokens (the chunk grouping is then the same).

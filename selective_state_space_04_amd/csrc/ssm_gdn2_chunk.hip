@@ -12,15 +12,19 @@
 //   vn = M^{-1} (w * v - BKe S)          (the corrected values)
 //   o  = scale (P vn + Qe S)
 //   S' = diag(exp(G_last)) S + Kd^T vn
-// Every exp(G_i - G_j) used has i >= j, so it is <= 1 for log-decays <= 0: the
-// decays are formed directly per element, never split into exp(G_i) and
-// exp(-G_j), so no gate strength can overflow them.
+// Every exp(G_i - G_j) used has i >= j, so it is <= 1 for log-decays <= 0.  It
+// is never split into exp(G_i) and exp(-G_j) (the second overflows for strong
+// gates): inside a 16-token diagonal block it is formed per element, and for
+// i, j in blocks bi > bj it is split at the end E of block bj as
+// exp(G_i - E) * exp(E - G_j), both factors <= 1, so no gate strength can
+// overflow it.
 //
 // Two kernels:
-//   k_gdn2_wy     key side, parallel over (pair, chunk): G, A and P (VALU, the
-//                 exp per element), M^{-1} by forward substitution, BKe, Qe,
-//                 Kd, exp(G_last); everything written to the workspace in the
-//                 operand order of v_mfma_f32_16x16x4f32.
+//   k_gdn2_wy     key side, parallel over (pair, chunk): G, A and P (the
+//                 off-diagonal 16-token blocks as MFMA products of the split
+//                 decays, the diagonal blocks per element), M^{-1} by forward
+//                 substitution, BKe, Qe, Kd, exp(G_last); everything written to
+//                 the workspace in the operand order of v_mfma_f32_16x16x4f32.
 //   k_gdn2_state  one workgroup per (pair, 16 state columns), sequential over
 //                 the chunks, its waves splitting the state's key rows: the
 //                 five products above on MFMA, the state in registers.  The 16
