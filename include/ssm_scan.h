@@ -127,8 +127,10 @@ enum {
 /* Name of a kernel id (for matching profiler output); "?" if unknown. */
 const char *ssm_kernel_name(int32_t kernel_id);
 
-/* Human-readable status. Never NULL. */
-const char *ssm_status_str(ssm_status s);
+/* Human-readable text of a status code (an ssm_status value, taken as a plain
+ * 32-bit integer so that any code, known or not, is a valid argument); "unknown
+ * status" for codes outside the enum.  Never NULL. */
+const char *ssm_status_str(int32_t status);
 
 /* Bytes of the checkpoint buffer a training forward writes and the backward
  * reads (f32 states at a fixed token stride; the layout is private to the

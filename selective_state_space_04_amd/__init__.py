@@ -67,7 +67,7 @@ def _load_library():
     P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     DP = ctypes.POINTER(SsmDims)
     TP = ctypes.POINTER(SsmTiming)
-    lib.ssm_status_str.argtypes = [ctypes.c_int]
+    lib.ssm_status_str.argtypes = [ctypes.c_int32]
     lib.ssm_status_str.restype = ctypes.c_char_p
     lib.ssm_kernel_name.argtypes = [I32]
     lib.ssm_kernel_name.restype = ctypes.c_char_p

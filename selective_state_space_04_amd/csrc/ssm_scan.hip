@@ -1006,8 +1006,8 @@ ssm_status run_bwd(const Plan& p, const void* x, const void* dt, const void* B, 
 // ===================================================================== C ABI
 extern "C" {
 
-const char* ssm_status_str(ssm_status s) {
-    switch (s) {
+const char* ssm_status_str(int32_t status) {
+    switch (status) {
         case SSM_OK: return "ok";
         case SSM_E_NULLPTR: return "required pointer is NULL";
         case SSM_E_SHAPE: return "dimension out of range";
