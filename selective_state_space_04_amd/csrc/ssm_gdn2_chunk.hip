@@ -26,10 +26,9 @@
 //                 substitution, BKe, Qe, Kd, exp(G_last); everything written to
 //                 the workspace in the operand order of v_mfma_f32_16x16x4f32.
 //   k_gdn2_state  one workgroup per (pair, 16 state columns), sequential over
-//                 the chunks, its waves splitting the state's key rows: the
-//                 five products above on MFMA, the state in registers.  The 16
-//                 columns of a pair run on one XCD, so its L2 serves their
-//                 shared key-side reads.
+//                 the chunks, one wave per 16-token tile: the five products
+//                 above on MFMA, the state in LDS.  The 16 columns of a pair
+//                 run on one XCD, so its L2 serves their shared key-side reads.
 // MFMA lane layout (v_mfma_f32_16x16x4f32, one wave): A[i][k] comes from lane
 // 16k + i, B[k][j] from lane 16k + j, and D[4q + r][j] lands in lane 16q + j,
 // register r.
@@ -298,225 +297,161 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// State pass: one workgroup per (pair, 16 columns of V), its NW waves each
-// holding a quarter (NW = 4) of the state's key rows.  Per chunk:
-//   1. each wave contracts its key rows: partial X = -BKe S (wave 0 adds w * v)
-//      and partial oq = Qe S, for all 64 tokens;
-//   2. (barrier) each wave sums the partials (fixed order) it needs and forms
-//      vn = M^{-1} X for its 16-token tiles;
-//   3. (barrier) every wave reads all of vn: o = scale (P vn + oq) for its
-//      tiles, and its key rows of S' = diag(exp(G_last)) S + Kd^T vn.
-// Partials, vn and the state's layout change go through LDS in [tile][r][lane]
-// rows padded to 68 floats (the B-operand reads then touch 64 distinct banks).
-// Every LDS region is read only between the barriers that follow its writes,
-// so one buffer of each suffices.
-template <int K> struct StateSplit {
-    static constexpr int NW = K / 16 < 4 ? K / 16 : 4;  // waves; each holds K / NW key rows
-    static constexpr int KW = K / NW;                   // key rows per wave
-    static constexpr int KBW = KW / 4;                  // k-blocks per wave (a multiple of 4)
-    static constexpr int TPW = 4 / NW;                  // 16-token tiles per wave
-    static_assert(KBW % 4 == 0 && KW % 16 == 0, "a wave's key rows must be whole float4 operand groups");
-};
-constexpr int RW = 68;  // padded LDS row: 64 lanes + 4
+// State pass: one workgroup of 4 waves per (pair, 16 columns of V), the
+// [K, 16] state in LDS.  Per chunk:
+//   1. wave w contracts tile w (tokens 16w .. 16w + 15) over all keys:
+//      X = w * v - BKe S and oq = Qe S, the state's operand blocks read from LDS;
+//   2. (barrier) every wave reads the X tiles up to its own and forms vn = M^{-1} X
+//      for its tile;
+//   3. (barrier) every wave reads all of vn: o = scale (P vn + oq) for its tile,
+//      and S' = diag(exp(G_last)) S + Kd^T vn for its quarter of the key rows;
+//   4. (barrier) the updated state is complete for the next chunk.
+constexpr int RW = 80;  // padded LDS row: 64 lanes + 16 (B-operand reads hit 64 banks)
 
 template <typename TT, int K>
-__global__ __launch_bounds__(StateSplit<K>::NW * 64) void k_gdn2_state(
+__global__ __launch_bounds__(256) void k_gdn2_state(
     const TT* __restrict__ v, const TT* __restrict__ w, const float* __restrict__ ws,
     const float* __restrict__ S0, float scale, TT* __restrict__ o, float* __restrict__ S_last, int64_t nbh,
     int64_t nbh8, int T, int V, int nch) {
     using L = Lay<K>;
-    using SP = StateSplit<K>;
-    constexpr int NW = SP::NW, KW = SP::KW, KBW = SP::KBW, TPW = SP::TPW;
-    constexpr int KB = K / 4;
-    __shared__ float xp[NW][4][4][RW];   // partial X per wave: [tile][r][lane]
-    __shared__ float oqp[NW][4][4][RW];  // partial Qe S per wave
-    __shared__ float vs[4][4][RW];       // vn
-    __shared__ float ss[NW][KW / 16][4][RW];  // per wave: Kd^T vn for its key rows
+    constexpr int KB = K / 4;                            // k-blocks of the contraction over keys
+    constexpr int NTK = K / 16;                          // 16-row tiles of the state
+    constexpr int TKW = NTK < 4 ? 1 : NTK / 4;           // state tiles per updating wave
+    __shared__ float Sl[K][16];                          // the state
+    __shared__ float xs[4][4][RW];                       // X as [tile][r][lane]
+    __shared__ float vs[4][4][RW];                       // vn
     const int l = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t pair = blockIdx.x % nbh8;  // a pair's column blocks share blockIdx % 8, hence an XCD
+    const int64_t pair = blockIdx.x % nbh8;
     const int cb = (int)(blockIdx.x / nbh8);
-    if (pair >= nbh) return;  // uniform over the workgroup: no barrier is skipped by part of it
+    if (pair >= nbh) return;  // uniform over the workgroup
     const int c16 = l & 15, quad = l >> 4;
     const int col = cb * 16 + c16;
-    const int key0 = wv * KW;  // this wave's first key row
-    // this wave's key rows of the state as the B operand: Skb[m] = S[key0 + 4m + quad][col]
-    float Skb[KBW];
-#pragma unroll
-    for (int m = 0; m < KBW; ++m) Skb[m] = S0 ? S0[(pair * K + key0 + 4 * m + quad) * V + col] : 0.0f;
-    // phase-1 operands of the next chunk are fetched during the current one
-    f4 pax[KBW / 4][4], paq[KBW / 4][4];
+    const bool upd = wv * TKW < NTK;  // this wave updates state tiles wv*TKW ..
+    for (int e = threadIdx.x; e < K * 16; e += 256) {
+        const int kr = e / 16, cc = e % 16;
+        Sl[kr][cc] = S0 ? S0[(pair * K + kr) * V + cb * 16 + cc] : 0.0f;
+    }
+    // this wave's tile of the key-side operands for the next chunk, fetched a chunk ahead
+    f4 pax[KB / 4], paq[KB / 4];
     {
         const float* b0 = ws + (pair * nch) * (int64_t)L::total;
 #pragma unroll
-        for (int g4 = 0; g4 < KBW / 4; ++g4)
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                pax[g4][ti] = opnd(b0 + L::nBKe, ti, wv * (KBW / 4) + g4, l, KB);
-                paq[g4][ti] = opnd(b0 + L::Qe, ti, wv * (KBW / 4) + g4, l, KB);
-            }
+        for (int m4 = 0; m4 < KB / 4; ++m4) {
+            pax[m4] = opnd(b0 + L::nBKe, wv, m4, l, KB);
+            paq[m4] = opnd(b0 + L::Qe, wv, m4, l, KB);
+        }
     }
-    // A chunk's outputs are stored after the next chunk's first loads have been
-    // issued: loads and stores retire in order, so a load issued after a store
-    // would also wait for that store.
-    f4 po[TPW];
+    f4 po = f4{0.0f, 0.0f, 0.0f, 0.0f};
     int pt0 = -1;
     auto store_o = [&]() {
         if (pt0 < 0) return;
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = pt0 + 16 * (wv * TPW + j) + 4 * quad + r;
-                if (tok < T) o[(pair * T + tok) * V + col] = ssm::from_f<TT>(scale * po[j][r]);
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int tok = pt0 + 16 * wv + 4 * quad + r;
+            if (tok < T) o[(pair * T + tok) * V + col] = ssm::from_f<TT>(scale * po[r]);
+        }
     };
+    __syncthreads();
     for (int c = 0; c < nch; ++c) {
         const float* base = ws + (pair * nch + c) * (int64_t)L::total;
         const float* nbase = ws + (pair * nch + min(c + 1, nch - 1)) * (int64_t)L::total;
         const int t0 = c * CH;
-        const int ti0 = wv * TPW;
-        // the later phases' operands are fetched first, so that their latency
-        // overlaps the first contractions (the barriers keep loads from moving)
-        f4 mi[TPW][4], pp[TPW][4], kd[KW / 16][4];
-        float eg[KBW];
+        // later phases' operands first
+        f4 mi[4], pp[4], kd[TKW][4];
+        float eg[TKW][4];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                const int ti = ti0 + j;
-                if (m4 <= ti) {
-                    mi[j][m4] = opnd(base + L::Mi, ti, m4, l, 16);
-                    pp[j][m4] = opnd(base + L::P, ti, m4, l, 16);
-                } else {
-                    mi[j][m4] = pp[j][m4] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-                }
+        for (int m4 = 0; m4 < 4; ++m4) {
+            if (m4 <= wv) {
+                mi[m4] = opnd(base + L::Mi, wv, m4, l, 16);
+                pp[m4] = opnd(base + L::P, wv, m4, l, 16);
+            } else {
+                mi[m4] = pp[m4] = f4{0.0f, 0.0f, 0.0f, 0.0f};
             }
-#pragma unroll
-        for (int tk = 0; tk < KW / 16; ++tk)
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) kd[tk][m4] = opnd(base + L::KdT, wv * (KW / 16) + tk, m4, l, 16);
-#pragma unroll
-        for (int m = 0; m < KBW; ++m) eg[m] = base[L::eGl + key0 + 4 * m + quad];
-        // 1. partial contractions over this wave's key rows
-        f4 X[4], oq[4];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = t0 + 16 * ti + 4 * quad + r;
-                const int64_t e = (pair * T + min(tok, T - 1)) * V + col;
-                X[ti][r] = (wv == 0 && tok < T) ? ld(w, e) * ld(v, e) : 0.0f;
-                oq[ti][r] = 0.0f;
-            }
-        store_o();  // the previous chunk's outputs
-#pragma unroll
-        for (int g4 = 0; g4 < KBW / 4; ++g4) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    X[ti] = mfma(pax[g4][ti][u], Skb[4 * g4 + u], X[ti]);
-                    oq[ti] = mfma(paq[g4][ti][u], Skb[4 * g4 + u], oq[ti]);
-                }
         }
 #pragma unroll
-        for (int g4 = 0; g4 < KBW / 4; ++g4)
+        for (int j = 0; j < TKW; ++j) {
+            const int tk = upd ? wv * TKW + j : 0;
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                pax[g4][ti] = opnd(nbase + L::nBKe, ti, wv * (KBW / 4) + g4, l, KB);
-                paq[g4][ti] = opnd(nbase + L::Qe, ti, wv * (KBW / 4) + g4, l, KB);
+            for (int m4 = 0; m4 < 4; ++m4) kd[j][m4] = opnd(base + L::KdT, tk, m4, l, 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) eg[j][r] = base[L::eGl + 16 * tk + 4 * quad + r];
+        }
+        f4 X = f4{0.0f, 0.0f, 0.0f, 0.0f}, oq = X;
+        float wvv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = t0 + 16 * wv + 4 * quad + r;
+            const int64_t e = (pair * T + min(tok, T - 1)) * V + col;
+            wvv[r] = tok < T ? ld(w, e) * ld(v, e) : 0.0f;
+        }
+        store_o();  // the previous chunk's outputs, after this chunk's first loads
+        // 1. tile wv over all keys; the state's operand block m is S[4m + quad][c16]
+#pragma unroll
+        for (int m4 = 0; m4 < KB / 4; ++m4)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float sb = Sl[4 * (4 * m4 + u) + quad][c16];
+                X = mfma(pax[m4][u], sb, X);
+                oq = mfma(paq[m4][u], sb, oq);
             }
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+        for (int m4 = 0; m4 < KB / 4; ++m4) {
+            pax[m4] = opnd(nbase + L::nBKe, wv, m4, l, KB);
+            paq[m4] = opnd(nbase + L::Qe, wv, m4, l, KB);
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                xp[wv][ti][r][l] = X[ti][r];
-                oqp[wv][ti][r][l] = oq[ti][r];
-            }
+        for (int r = 0; r < 4; ++r) xs[wv][r][l] = X[r] + wvv[r];
         __syncthreads();
-        // 2. vn = M^{-1} X for this wave's tiles (lower triangular: token blocks
-        // up to the last tile's end), and the summed Qe S of those tiles
-        constexpr int MJ = 4 * TPW;  // token blocks the last tile needs, per wave index
+        // 2. vn for this tile from the X tiles up to it
         float Xkb[16];
 #pragma unroll
-        for (int mj = 0; mj < 16; ++mj) {
-            if (mj < 4 * ti0 + MJ) {
-                float sx = 0.0f;
+        for (int mj = 0; mj < 16; ++mj) Xkb[mj] = mj < 4 * wv + 4 ? xs[mj / 4][quad][16 * (mj % 4) + c16] : 0.0f;
+        f4 vn = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int p = 0; p < NW; ++p) sx += xp[p][mj / 4][quad][16 * (mj % 4) + c16];
-                Xkb[mj] = sx;
-            } else {
-                Xkb[mj] = 0.0f;
-            }
-        }
-        f4 vn[TPW], oqt[TPW];
+        for (int m4 = 0; m4 < 4; ++m4)
+            if (m4 <= wv) {
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int ti = ti0 + j;
-            vn[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                if (m4 <= ti) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) vn[j] = mfma(mi[j][m4][u], Xkb[4 * m4 + u], vn[j]);
-                }
+                for (int u = 0; u < 4; ++u) vn = mfma(mi[m4][u], Xkb[4 * m4 + u], vn);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float so = 0.0f;
-#pragma unroll
-                for (int p = 0; p < NW; ++p) so += oqp[p][ti][r][l];
-                oqt[j][r] = so;
-                vs[ti][r][l] = vn[j][r];
-            }
-        }
+        for (int r = 0; r < 4; ++r) vs[wv][r][l] = vn[r];
         __syncthreads();
-        // 3. every wave reads all of vn
+        // 3. outputs of this tile and this wave's rows of the new state
         float vkb[16];
 #pragma unroll
         for (int mj = 0; mj < 16; ++mj) vkb[mj] = vs[mj / 4][quad][16 * (mj % 4) + c16];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int ti = ti0 + j;
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                if (m4 <= ti) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) oqt[j] = mfma(pp[j][m4][u], vkb[4 * m4 + u], oqt[j]);
-                }
-            }
-        }
-        f4 sn[KW / 16];
-#pragma unroll
-        for (int tk = 0; tk < KW / 16; ++tk) sn[tk] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
         for (int m4 = 0; m4 < 4; ++m4)
+            if (m4 <= wv) {
 #pragma unroll
-            for (int tk = 0; tk < KW / 16; ++tk) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) sn[tk] = mfma(kd[tk][m4][u], vkb[4 * m4 + u], sn[tk]);
+                for (int u = 0; u < 4; ++u) oq = mfma(pp[m4][u], vkb[4 * m4 + u], oq);
             }
-#pragma unroll
-        for (int tk = 0; tk < KW / 16; ++tk)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ss[wv][tk][r][l] = sn[tk][r];
-        wave_sync_lds();
-#pragma unroll
-        for (int m = 0; m < KBW; ++m) {
-            const int kl = 4 * m + quad;  // key row within this wave's rows
-            const float add = ss[wv][kl / 16][kl % 4][16 * ((kl % 16) / 4) + c16];
-            Skb[m] = __builtin_fmaf(eg[m], Skb[m], add);
-        }
-        wave_sync_lds();
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) po[j] = oqt[j];
+        po = oq;
         pt0 = t0;
+        if (upd) {
+#pragma unroll
+            for (int j = 0; j < TKW; ++j) {
+                const int tk = wv * TKW + j;
+                f4 sn;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sn[r] = eg[j][r] * Sl[16 * tk + 4 * quad + r][c16];
+#pragma unroll
+                for (int m4 = 0; m4 < 4; ++m4)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) sn = mfma(kd[j][m4][u], vkb[4 * m4 + u], sn);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sl[16 * tk + 4 * quad + r][c16] = sn[r];
+            }
+        }
+        __syncthreads();
     }
     store_o();
     if (S_last) {
-#pragma unroll
-        for (int m = 0; m < KBW; ++m) S_last[(pair * K + key0 + 4 * m + quad) * V + col] = Skb[m];
+        for (int e = threadIdx.x; e < K * 16; e += 256) {
+            const int kr = e / 16, cc = e % 16;
+            S_last[(pair * K + kr) * V + cb * 16 + cc] = Sl[kr][cc];
+        }
     }
 }
 
@@ -559,7 +494,7 @@ ssm_status run(const ssm_gdn2_dims* d, const void* q, const void* k, const void*
                    (const TT*)k, (const TT*)g, (const TT*)b, ws, T, nch));
     const int64_t nbh8 = (nbh + XCDS - 1) / XCDS * XCDS;
     return launch(SSM_K_GDN2_STATE, k_gdn2_state<TT, K>, dim3((unsigned)(nbh8 * (V / 16))),
-                  dim3(StateSplit<K>::NW * 64), (const TT*)v,
+                  dim3(256), (const TT*)v,
                   (const TT*)w, (const float*)ws, S0, scale, (TT*)o, S_last, nbh, nbh8, T, V, nch);
 }
 
