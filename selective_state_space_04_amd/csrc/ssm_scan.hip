@@ -84,6 +84,46 @@ __device__ __forceinline__ void load16(const bf16_t* __restrict__ p, float v[NS]
     }
 }
 
+// A 16-value row (B_t or C_t) loaded now and converted to f32 later, so that
+// the wait for it can come a token after the load was issued.
+template <typename T>
+struct RawRow;
+template <>
+struct RawRow<float> {
+    float4 q[4];
+    __device__ __forceinline__ void load(const float* __restrict__ p) {
+        const float4* s = reinterpret_cast<const float4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = s[i];
+    }
+    __device__ __forceinline__ void get(float v[NS]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[4 * i + 0] = q[i].x; v[4 * i + 1] = q[i].y; v[4 * i + 2] = q[i].z; v[4 * i + 3] = q[i].w;
+        }
+    }
+};
+template <>
+struct RawRow<bf16_t> {
+    uint4 q[2];
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ p) {
+        const uint4* s = reinterpret_cast<const uint4*>(p);
+        q[0] = s[0];
+        q[1] = s[1];
+    }
+    __device__ __forceinline__ void get(float v[NS]) const {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
+                v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            }
+        }
+    }
+};
+
 __device__ __forceinline__ void load_state(const float* __restrict__ p, float h[NS]) {
     const float4* q = reinterpret_cast<const float4*>(p);
 #pragma unroll
@@ -473,6 +513,12 @@ __global__ __launch_bounds__(WG) void k_bwd_carry(
 //     wave sums column (q mod 32) over half of the 64 rows; the 2 halves x 4
 //     waves are summed after the block and written as one partial per
 //     (token, workgroup).
+//     Latency: at 2 waves per SIMD (the TS x NS states take most of the 256
+//     VGPRs) little else hides a wait, so a block's x and dt are fetched
+//     together with its checkpoint, B_t rows a token ahead of their use, C_t
+//     rows touched during the recompute (the reverse sweep then finds them in
+//     the scalar cache), dy and z two tokens ahead, and x kept in LDS for the
+//     reverse sweep instead of being read again.
 template <typename T, bool GATE>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_main(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
@@ -488,6 +534,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     __shared__ float rows[NWAVE][64 * RS];
     __shared__ float wres[TS][2 * NWAVE][32];
     __shared__ float2 dsg[NWAVE][TS][64];  // per token: delta, sigmoid(dt + dt_bias)
+    __shared__ float xsl[NWAVE][TS][64];   // per token: x
     const int d = blockIdx.x * WG + threadIdx.x;
     const int k = blockIdx.y;
     const int b = blockIdx.z;
@@ -535,33 +582,51 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int64_t row0 = (int64_t)b * L + ts;
         const float* ckp = ckpt + (((int64_t)b * nck + j) * D + dc) * NS;
         float hc[TS][NS];  // state after token ts+i
-        // first token of the reverse sweep, fetched early
-        T xn, gn, zn = T(0);
-        {
-            const int64_t rl = (row0 + cnt - 1) * D + dc;
-            xn = x[rl];
-            gn = dy[rl];
-            if (GATE) zn = z[rl];
+        // dy, z of the first RP tokens of the reverse sweep, fetched early
+        constexpr int RP = 2;
+        T gq[RP], zq[RP];
+#pragma unroll
+        for (int q = 0; q < RP; ++q) {
+            const int64_t rl = (row0 + max(cnt - 1 - q, 0)) * D + dc;
+            gq[q] = dy[rl];
+            zq[q] = GATE ? z[rl] : T(0);
         }
         {
             float hs[NS];
             load_state(ckp, hs);
-            T xr = x[row0 * D + dc], dr = dt[row0 * D + dc];
+            T xr[TS], dr[TS];  // the block's x and dt, all fetched at once
+#pragma unroll
+            for (int i = 0; i < TS; ++i) {
+                const int64_t rr = (row0 + min(i, cnt - 1)) * D + dc;
+                xr[i] = x[rr];
+                dr[i] = dt[rr];
+            }
             flush();  // the previous block's deferred stores
+            // B_t one token ahead; C_t touched one token ahead (its first word is
+            // consumed a token later, so the load is kept but not waited for early)
+            // so that the reverse sweep finds the row in the scalar cache.  The
+            // next row is clamped into the block rather than skipped: a
+            // conditional load would leave a copy that waits for it at once.
+            RawRow<T> bn;
+            bn.load(Bm + row0 * NS);
+            uint32_t cw = *reinterpret_cast<const uint32_t*>(Cm + row0 * NS);
 #pragma unroll
             for (int i = 0; i < TS; ++i) {
                 if (i < cnt) {
                     const int64_t row = row0 + i;
-                    const float xv = to_f(xr), dtv = to_f(dr);
-                    if (i + 1 < cnt) {  // next token, one ahead
-                        xr = x[(row + 1) * D + dc];
-                        dr = dt[(row + 1) * D + dc];
-                    }
+                    const float xv = to_f(xr[i]), dtv = to_f(dr[i]);
                     float Bv[NS];
-                    load16(Bm + row * NS, Bv);
+                    bn.get(Bv);
+                    asm volatile("" ::"s"(cw));
+                    {
+                        const int64_t rn = row0 + min(i + 1, cnt - 1);  // in bounds
+                        bn.load(Bm + rn * NS);
+                        cw = *reinterpret_cast<const uint32_t*>(Cm + rn * NS);
+                    }
                     float sg;
                     const float delta = softplus_sig(dtv + bias, sg);
                     dsg[wave][i][lane] = make_float2(delta, sg);
+                    xsl[wave][i][lane] = xv;
                     const float dxv = delta * xv;
 #pragma unroll
                     for (int n = 0; n < NS; ++n) {
@@ -581,15 +646,19 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         for (int i = TS - 1; i >= 0; --i) {
             if (i < cnt) {
                 const int64_t row = row0 + i;
-                const float xv = to_f(xn);
-                const float dyv = to_f(gn);
+                const float xv = xsl[wave][i][lane];
+                const float dyv = to_f(gq[0]);
                 float zv = 0.0f, sz = 0.0f, g = dyv;
-                if (GATE) zv = to_f(zn);
-                if (i > 0) {
-                    const int64_t rp = (row - 1) * D + dc;
-                    xn = x[rp];
-                    gn = __builtin_nontemporal_load(&dy[rp]);
-                    if (GATE) zn = __builtin_nontemporal_load(&z[rp]);
+                if (GATE) zv = to_f(zq[0]);
+#pragma unroll
+                for (int q = 0; q + 1 < RP; ++q) {
+                    gq[q] = gq[q + 1];
+                    zq[q] = zq[q + 1];
+                }
+                if (i >= RP) {  // token i - RP, RP tokens ahead
+                    const int64_t rp = (row - RP) * D + dc;
+                    gq[RP - 1] = __builtin_nontemporal_load(&dy[rp]);
+                    if (GATE) zq[RP - 1] = __builtin_nontemporal_load(&z[rp]);
                 }
                 if (GATE) {
                     sz = sigmoid_f(zv);
@@ -635,7 +704,13 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                     float sacc = 0.0f;
 #pragma unroll
-                    for (int r = 0; r < 32; ++r) sacc += colp[r * RS];
+                    for (int r0 = 0; r0 < 32; r0 += 8) {  // 8 reads in flight, then the adds in row order
+                        float cv[8];
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) cv[r] = colp[(r0 + r) * RS];
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) sacc += cv[r];
+                    }
                     wres[i][2 * wave + half][col] = sacc;
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                     __builtin_amdgcn_wave_barrier();
