@@ -636,12 +636,12 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 }
             }
         }
-        // Activations of the next (earlier) token are fetched before this token's
-        // stores are issued: loads and stores retire in order, so a load issued
-        // after a store would also wait for that store.  dy and z are read once and
-        // dx, ddt, dz written once: non-temporal, so that this streaming traffic
-        // does not push the block's checkpoint (read again at its first token)
-        // out of L2.
+        // dy and z of the token two ahead (earlier in time) are fetched before
+        // this token's stores are issued: loads and stores retire in order, so a
+        // load issued after a store would also wait for that store.  dy and z are
+        // read once and dx, ddt, dz written once: non-temporal, so that this
+        // streaming traffic does not push the block's checkpoint (read again at
+        // its first token) out of L2.
 #pragma unroll
         for (int i = TS - 1; i >= 0; --i) {
             if (i < cnt) {

@@ -245,9 +245,12 @@ def test_g2_random_a_log():
     _check_all(inp)
 
 
-@pytest.mark.parametrize("L", [1, 63, 1000])
+@pytest.mark.parametrize("L", [1, 2, 63, 258, 1000])
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
 def test_g3_ragged(L, io):
+    """Sequences whose last 8-token checkpoint block holds 1, 2, 7, 2 and 8 tokens
+    (the backward fetches a block's rows clamped into the block, and dy, z two
+    tokens ahead)."""
     bf = io == torch.bfloat16
     inp = W.make_inputs(3, L, 100, seed=13 + L, bf16=bf)
     tol = (BF16_TOL, BF16_TOL) if bf else (F32_FWD, F32_GRAD)
