@@ -826,33 +826,37 @@ def cpu_scan_baseline(inp, cfg, passes, budget_s=12.0):
     N = cfg["d_state"]
     bwd = "bwd" in passes
 
-    def run(rows):
+    def run(rows):  # (seconds for the whole pass, seconds for its forward)
         sub = {k: inp[k][:rows] for k in ("x", "z", "dt", "B", "C") + (("dy",) if bwd else ())}
         t0 = time.perf_counter()
         oracle.fwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"], inp["A_log"], inp["D"], inp["dt_bias"])
+        t1 = time.perf_counter()
         if bwd:
             oracle.bwd(sub["x"], sub["dt"], sub["B"], sub["C"], sub["z"], inp["A_log"], inp["D"], inp["dt_bias"],
                        sub["dy"])
-        return time.perf_counter() - t0
+        return time.perf_counter() - t0, t1 - t0
 
-    sec1 = run(1)
-    per_row = max(sec1, 1e-6)
+    per_row = max(run(1)[0], 1e-6)
     if per_row * bsz <= budget_s:
         # the whole workload, repeated until at least 10 s of host work
-        reps, sec = 0, 0.0
+        reps, sec, fsec = 0, 0.0, 0.0
         while reps < 100000 and sec < 10.0:
-            sec += run(bsz)
+            a, f = run(bsz)
+            sec, fsec = sec + a, fsec + f
             reps += 1
         rows, what = bsz, f"the whole workload ({bsz} rows), {reps} run(s)"
     else:
         rows = max(1, min(bsz, int(budget_s / per_row)))
         reps = 1
-        sec = run(rows)
+        sec, fsec = run(rows)
         what = f"batch rows 0..{rows - 1} of {bsz}, all {L} tokens and {D} channels"
     elems = reps * rows * L * D * N
-    return {"value": elems / sec, "unit": "elements/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{what}, {'fwd+bwd' if bwd else 'fwd'} in f64 ({elems} elements, {sec:.1f} s)",
-            **host_cpu()}
+    out = {"value": elems / sec, "unit": "elements/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"{what}, {'fwd+bwd' if bwd else 'fwd'} in f64 ({elems} elements, {sec:.1f} s)",
+           **host_cpu()}
+    if bwd:  # the same runs' forward alone
+        out["fwd_value"] = elems / fsec
+    return out
 
 
 def scan_bench(args):
@@ -883,9 +887,11 @@ def scan_bench(args):
              "ddt_bias": torch.empty_like(t["dt_bias"]), "dh0": None}
     y = torch.empty_like(t["x"])
 
-    def step(timer=None):
+    def step(timer=None, mid=None):
         _, _, ckpt = ssm.ssm_scan_fwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"],
                                       t["dt_bias"], training=bwd, y=y, timing=timer)
+        if mid is not None:
+            mid.record()
         if bwd:
             ssm.ssm_scan_bwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"], ckpt,
                              t["dy"], out=grads, timing=timer)
@@ -901,15 +907,17 @@ def scan_bench(args):
     # every step starts from cold caches.
     flush = CacheFlush(dev)
     timers = [ssm.LaunchTimer() for _ in range(args.steps)]
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         flush()
         ev[i][0].record()
-        step(timers[i])
-        ev[i][1].record()
+        step(timers[i], mid=ev[i][1])
+        ev[i][2].record()
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+    fwd_ms = [a.elapsed_time(m) for a, m, _ in ev]
+    ms = float(np.mean(step_ms))
     # Unflushed: the same steps back to back.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -971,7 +979,13 @@ def scan_bench(args):
                                f"{cfg['io']} activations, f32 state, {work}",
                    "batch": bsz, "seqlen": L, "d_inner": D, "d_state": N, "io_dtype": cfg["io"], "passes": work},
         "timing": {"ms_per_step_flushed": round(ms, 4), "ms_per_step_unflushed": round(ms_hot, 4),
-                   "flush": "512 MiB read between timed steps, outside each step's events"},
+                   "ms_per_step_flushed_median": round(float(np.median(step_ms)), 4),
+                   "ms_fwd_flushed": round(float(np.mean(fwd_ms)), 4),
+                   "ms_bwd_flushed": round(float(np.mean([s - f for s, f in zip(step_ms, fwd_ms)])), 4)
+                   if bwd else None,
+                   "flush": "512 MiB read between timed steps, outside each step's events; the backward "
+                            "follows its forward without a flush"},
+        "inputs": {"generator": "numpy default_rng(seed) (PCG64)", "seed": 0, "numpy": np.__version__},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "frac_of_copy": round(step_bytes / (ms * 1e-3) / 1e9 / copy_gbps, 4)},
