@@ -827,63 +827,84 @@ __global__ __launch_bounds__(WG) void k_bwd_reduce_params(
 }
 
 // ======================================================================= step
-// One token for 256 channels of one batch row.  Each wave's 64 channels hold
-// 4 KB of contiguous state; it is moved between HBM and registers through LDS
-// so that every global load/store instruction covers 1 KB contiguously.
+// One token for 256 channels of SR consecutive batch rows.  Each wave's 64
+// channels hold 4 KB of contiguous state per row; it is moved between memory and
+// registers through LDS so that every global load/store instruction covers 1 KB
+// contiguously.  A wave walks its rows in turn: the decay rates are formed once
+// for all of them, and the next row's state and activations are loaded while
+// the current row is computed.
 template <typename T, bool GATE>
 __global__ __launch_bounds__(WG) void k_step(
     float* __restrict__ h, const T* __restrict__ x, const T* __restrict__ dt,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const T* __restrict__ z,
     const float* __restrict__ A_log, const float* __restrict__ Dp,
-    const float* __restrict__ dt_bias, T* __restrict__ y, int D) {
+    const float* __restrict__ dt_bias, T* __restrict__ y, int D, int Bt, int SR) {
     constexpr int HS = NS + 4;  // padded LDS row (16-byte aligned, conflict-free)
     __shared__ float hsm[NWAVE][64 * HS];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int d0 = blockIdx.x * WG + wave * 64;
     const int nvalid = min(64, D - d0);  // channels of this wave (uniform)
     if (nvalid <= 0) return;             // no block-wide barriers below
-    const int b = blockIdx.z;
+    const int b0 = blockIdx.z * SR, b1 = min(b0 + SR, Bt);
     const int d = d0 + lane;
     const bool act = lane < nvalid;
-    float* sm = hsm[wave];
-    float4* hb = reinterpret_cast<float4*>(h + ((int64_t)b * D + d0) * NS);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int pc = j * 64 + lane;  // 16-byte piece: channel pc/4, states 4*(pc%4)..
-        if ((pc >> 2) < nvalid)
-            *reinterpret_cast<float4*>(sm + (pc >> 2) * HS + (pc & 3) * 4) = hb[pc];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int dc = act ? d : d0;
+    float* sm = hsm[wave];
     float A2[NS];
     load_A2(A_log, dc, A2);
     const float bias = dt_bias ? dt_bias[dc] : 0.0f;
     const float Dd = Dp ? Dp[dc] : 0.0f;
-    const int64_t i = (int64_t)b * D + dc;
-    float hs[NS];
-    load_state(sm + (act ? lane : 0) * HS, hs);
-    float Bv[NS], Cv[NS];
-    load16(Bm + (int64_t)b * NS, Bv);
-    load16(Cm + (int64_t)b * NS, Cv);
-    const float xv = to_f(x[i]), dtv = to_f(dt[i]);
-    const float zv = GATE ? to_f(z[i]) : 0.0f;
-    float sg;
-    const float delta = softplus_sig(dtv + bias, sg);
-    const float acc = scan_token(hs, A2, Bv, Cv, delta, xv);
-    if (act) {
-        y[i] = from_f<T>(finish_y<GATE>(acc, Dd, xv, zv));
-        store_state(sm + lane * HS, hs);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // a row's state as 16-byte pieces (piece pc: channel pc/4, states 4*(pc%4)..)
+    // and its activations
+    float4 raw[4];
+    T xr, dr, zr = T(0);
+    auto fetch = [&](int b) {
+        const float4* hb = reinterpret_cast<const float4*>(h + ((int64_t)b * D + d0) * NS);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int pc = j * 64 + lane;
-        if ((pc >> 2) < nvalid)
-            hb[pc] = *reinterpret_cast<const float4*>(sm + (pc >> 2) * HS + (pc & 3) * 4);
+        for (int j = 0; j < 4; ++j) {
+            const int pc = j * 64 + lane;
+            raw[j] = (pc >> 2) < nvalid ? hb[pc] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+        const int64_t i = (int64_t)b * D + dc;
+        xr = x[i];
+        dr = dt[i];
+        if (GATE) zr = z[i];
+    };
+    fetch(b0);
+    for (int b = b0; b < b1; ++b) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pc = j * 64 + lane;
+            if ((pc >> 2) < nvalid) *reinterpret_cast<float4*>(sm + (pc >> 2) * HS + (pc & 3) * 4) = raw[j];
+        }
+        const float xv = to_f(xr), dtv = to_f(dr);
+        const float zv = GATE ? to_f(zr) : 0.0f;
+        float Bv[NS], Cv[NS];
+        load16(Bm + (int64_t)b * NS, Bv);
+        load16(Cm + (int64_t)b * NS, Cv);
+        if (b + 1 < b1) fetch(b + 1);  // the next row, while this one is computed
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float hs[NS];
+        load_state(sm + (act ? lane : 0) * HS, hs);
+        float sg;
+        const float delta = softplus_sig(dtv + bias, sg);
+        const float acc = scan_token(hs, A2, Bv, Cv, delta, xv);
+        const int64_t i = (int64_t)b * D + dc;
+        if (act) {
+            y[i] = from_f<T>(finish_y<GATE>(acc, Dd, xv, zv));
+            store_state(sm + lane * HS, hs);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float4* hb = reinterpret_cast<float4*>(h + ((int64_t)b * D + d0) * NS);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pc = j * 64 + lane;
+            if ((pc >> 2) < nvalid) hb[pc] = *reinterpret_cast<const float4*>(sm + (pc >> 2) * HS + (pc & 3) * 4);
+        }
     }
 }
 
@@ -1230,14 +1251,18 @@ ssm_status ssm_scan_step(int64_t batch, int64_t d_inner, int64_t d_state, int32_
         if (q && misaligned(q)) return SSM_E_ALIGN;
     (void)hipGetLastError();
     Launcher launch{{stream, timing}};
-    const dim3 grid((unsigned)((d_inner + WG - 1) / WG), 1, (unsigned)batch);
-    const int Dn = (int)d_inner;
+    // batch rows per wave: as many as still leave >= 4096 waves (4 per SIMD)
+    const int64_t ndb = (d_inner + WG - 1) / WG;
+    int SR = 1;
+    while (SR < 8 && ndb * NWAVE * ((batch + 2 * SR - 1) / (2 * SR)) >= 4096) SR *= 2;
+    const dim3 grid((unsigned)ndb, 1, (unsigned)((batch + SR - 1) / SR));
+    const int Dn = (int)d_inner, Bn = (int)batch;
     if (io_dtype == SSM_F32) {
-        return z ? launch(SSM_K_STEP, k_step<float, true>, grid, h, (const float*)x, (const float*)dt, (const float*)B, (const float*)C, (const float*)z, A_log, D, dt_bias, (float*)y, Dn)
-                 : launch(SSM_K_STEP, k_step<float, false>, grid, h, (const float*)x, (const float*)dt, (const float*)B, (const float*)C, (const float*)z, A_log, D, dt_bias, (float*)y, Dn);
+        return z ? launch(SSM_K_STEP, k_step<float, true>, grid, h, (const float*)x, (const float*)dt, (const float*)B, (const float*)C, (const float*)z, A_log, D, dt_bias, (float*)y, Dn, Bn, SR)
+                 : launch(SSM_K_STEP, k_step<float, false>, grid, h, (const float*)x, (const float*)dt, (const float*)B, (const float*)C, (const float*)z, A_log, D, dt_bias, (float*)y, Dn, Bn, SR);
     }
-    return z ? launch(SSM_K_STEP, k_step<bf16_t, true>, grid, h, (const bf16_t*)x, (const bf16_t*)dt, (const bf16_t*)B, (const bf16_t*)C, (const bf16_t*)z, A_log, D, dt_bias, (bf16_t*)y, Dn)
-             : launch(SSM_K_STEP, k_step<bf16_t, false>, grid, h, (const bf16_t*)x, (const bf16_t*)dt, (const bf16_t*)B, (const bf16_t*)C, (const bf16_t*)z, A_log, D, dt_bias, (bf16_t*)y, Dn);
+    return z ? launch(SSM_K_STEP, k_step<bf16_t, true>, grid, h, (const bf16_t*)x, (const bf16_t*)dt, (const bf16_t*)B, (const bf16_t*)C, (const bf16_t*)z, A_log, D, dt_bias, (bf16_t*)y, Dn, Bn, SR)
+             : launch(SSM_K_STEP, k_step<bf16_t, false>, grid, h, (const bf16_t*)x, (const bf16_t*)dt, (const bf16_t*)B, (const bf16_t*)C, (const bf16_t*)z, A_log, D, dt_bias, (bf16_t*)y, Dn, Bn, SR);
 }
 
 }  // extern "C"
