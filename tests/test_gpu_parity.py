@@ -362,6 +362,34 @@ def test_step_bf16_matches_forward():
     assert torch.equal(hs, h)
 
 
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("gate", [True, False])
+def test_step_row_groups_match_forward(io, gate):
+    """Steps at a width where a wave takes several batch rows in turn: batch 257
+    leaves a last group of one row, and d_inner 5100 a partly filled last wave.
+    Bit-identical to the forward, which runs this width as one sequential chunk."""
+    bf = io == torch.bfloat16
+    inp = W.make_inputs(257, 3, 5100, seed=23, bf16=bf, with_dy=False)
+    if not gate:
+        inp["z"] = None
+    t = {k: (_t(v, io) if k in ("x", "z", "dt", "B", "C") else _t(v)) for k, v in inp.items()
+         if v is not None}
+    z = t.get("z")
+    assert ssm.fwd_workspace_bytes(257, 3, 5100, io_dtype=io) == 0  # one sequential chunk
+    y, h, _ = ssm.ssm_scan_fwd(t["x"], t["dt"], t["B"], t["C"], z, t["A_log"], t["D"], t["dt_bias"],
+                               return_last_state=True)
+    hs = torch.zeros(257, 5100, 16, device=DEV)
+    ys = []
+    for s_ in range(3):
+        sl = {k: t[k][:, s_].contiguous() for k in ("x", "dt", "B", "C")}
+        zs = z[:, s_].contiguous() if z is not None else None
+        ys.append(ssm.ssm_scan_step(hs, sl["x"], sl["dt"], sl["B"], sl["C"], zs, t["A_log"], t["D"],
+                                    t["dt_bias"]))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(ys, 1), y)
+    assert torch.equal(hs, h)
+
+
 def test_bf16_outputs_are_nearest_even_roundings_of_the_f32_path():
     """With bf16-representable inputs the bf16-I/O kernels do the same f32
     arithmetic as the f32-I/O kernels; every stored bf16 output must be the
