@@ -786,43 +786,65 @@ __global__ __launch_bounds__(WG) void k_bwd_reduce_bc(const float* __restrict__ 
     else dC[row * NS + (v - NS)] = from_f<T>(s);
 }
 
-// dA_log = A * sum dA, dD, ddt_bias: fixed-order sums over (batch, chunk).
+// dA_log = A * sum dA, dD, ddt_bias: fixed-order sums over the (batch, chunk)
+// partials.  A workgroup takes RO outputs; its RG thread groups each sum a
+// contiguous run of the partials in order, and the RG run sums are then added
+// in run order (a fixed association, so the result is bitwise reproducible).
+// Splitting the runs puts RG times as many loads in flight as one sequential
+// sum per output, which at few outputs (small d_inner) was latency-bound.
+constexpr int RO = 32, RG = WG / RO;
 __global__ __launch_bounds__(WG) void k_bwd_reduce_params(
     const float* __restrict__ A_log, const float* __restrict__ wsPA,
     const float* __restrict__ wsPD, float* __restrict__ dA_log, float* __restrict__ dDo,
     float* __restrict__ ddt_bias, int Bt, int K, int D) {
+    __shared__ float2 red[RG][RO];
     const int64_t DN = (int64_t)D * NS;
-    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
-    const int64_t J = (int64_t)Bt * K;  // partials, summed in (batch, chunk) order
+    const int o = threadIdx.x % RO, g = threadIdx.x / RO;
+    const int64_t i = (int64_t)blockIdx.x * RO + o;  // dA outputs [0, DN), then (dD, ddt_bias) [DN, DN + D)
+    const int64_t J = (int64_t)Bt * K;               // partials, in (batch, chunk) order
+    const int64_t jb = J * g / RG, je = J * (g + 1) / RG;
+    float s0 = 0.0f, s1 = 0.0f;
     if (i < DN) {
-        float s = 0.0f;
-        for (int64_t j0 = 0; j0 < J; j0 += CB) {  // CB loads in flight, then the adds in order
+        for (int64_t j0 = jb; j0 < je; j0 += CB) {  // CB loads in flight, then the adds in order
             float v[CB];
 #pragma unroll
             for (int j = 0; j < CB; ++j)
-                if (j0 + j < J) v[j] = wsPA[(j0 + j) * DN + i];
+                if (j0 + j < je) v[j] = wsPA[(j0 + j) * DN + i];
 #pragma unroll
             for (int j = 0; j < CB; ++j)
-                if (j0 + j < J) s += v[j];
+                if (j0 + j < je) s0 += v[j];
         }
-        dA_log[i] = s * -expf(A_log[i]);
     } else if (i < DN + D) {
         const int64_t d = i - DN;
-        float s0 = 0.0f, s1 = 0.0f;
-        for (int64_t j0 = 0; j0 < J; j0 += CB) {
+        for (int64_t j0 = jb; j0 < je; j0 += CB) {
             float2 v[CB];
 #pragma unroll
             for (int j = 0; j < CB; ++j)
-                if (j0 + j < J) v[j] = reinterpret_cast<const float2*>(wsPD)[(j0 + j) * D + d];
+                if (j0 + j < je) v[j] = reinterpret_cast<const float2*>(wsPD)[(j0 + j) * D + d];
 #pragma unroll
             for (int j = 0; j < CB; ++j)
-                if (j0 + j < J) {
+                if (j0 + j < je) {
                     s0 += v[j].x;
                     s1 += v[j].y;
                 }
         }
-        if (dDo) dDo[d] = s0;
-        ddt_bias[d] = s1;
+    }
+    red[g][o] = make_float2(s0, s1);
+    __syncthreads();
+    if (g == 0) {
+        float2 t = red[0][o];
+#pragma unroll
+        for (int r = 1; r < RG; ++r) {
+            t.x += red[r][o].x;
+            t.y += red[r][o].y;
+        }
+        if (i < DN) {
+            dA_log[i] = t.x * -expf(A_log[i]);
+        } else if (i < DN + D) {
+            const int64_t d = i - DN;
+            if (dDo) dDo[d] = t.x;
+            ddt_bias[d] = t.y;
+        }
     }
 }
 
@@ -1092,7 +1114,7 @@ ssm_status run_bwd(const Plan& p, const void* x, const void* dt, const void* B, 
     SSM_TRY(launch(SSM_K_BWD_REDUCE_BC, k_bwd_reduce_bc<T>, dim3((unsigned)((rows * 32 + WG - 1) / WG)),
                    (const float*)BC, (T*)dB, (T*)dC, rows, (int)p.ndb));
     const int64_t np = p.D * NS + p.D;
-    return launch(SSM_K_BWD_REDUCE_P, k_bwd_reduce_params, dim3((unsigned)((np + WG - 1) / WG)),
+    return launch(SSM_K_BWD_REDUCE_P, k_bwd_reduce_params, dim3((unsigned)((np + RO - 1) / RO)),
                   A_log, (const float*)PA, (const float*)PD, dA_log, dD, ddt_bias, (int)p.Bt,
                   (int)p.Kb, D);
 }
