@@ -1273,10 +1273,10 @@ ssm_status ssm_scan_step(int64_t batch, int64_t d_inner, int64_t d_state, int32_
         if (q && misaligned(q)) return SSM_E_ALIGN;
     (void)hipGetLastError();
     Launcher launch{{stream, timing}};
-    // batch rows per wave: as many as still leave >= 4096 waves (4 per SIMD)
+    // batch rows per wave: up to 4, as many as still leave >= 4096 waves (4 per SIMD)
     const int64_t ndb = (d_inner + WG - 1) / WG;
     int SR = 1;
-    while (SR < 8 && ndb * NWAVE * ((batch + 2 * SR - 1) / (2 * SR)) >= 4096) SR *= 2;
+    while (SR < 4 && ndb * NWAVE * ((batch + 2 * SR - 1) / (2 * SR)) >= 4096) SR *= 2;
     const dim3 grid((unsigned)ndb, 1, (unsigned)((batch + SR - 1) / SR));
     const int Dn = (int)d_inner, Bn = (int)batch;
     if (io_dtype == SSM_F32) {
