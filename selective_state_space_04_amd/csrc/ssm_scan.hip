@@ -132,6 +132,23 @@ __device__ __forceinline__ void load_state(const float* __restrict__ p, float h[
         h[4 * i + 0] = f.x; h[4 * i + 1] = f.y; h[4 * i + 2] = f.z; h[4 * i + 3] = f.w;
     }
 }
+// Grouped state rows: states 4g..4g+3 of channel d at base[(g * D + d) * 4 ..],
+// base wave-uniform.  Each of the 4 accesses moves 16 bytes per lane, and the
+// lanes of a wave (consecutive channels) cover one dense 1 KB piece.
+__device__ __forceinline__ void load_state_g4(const float* __restrict__ base, int64_t D, int64_t d,
+                                              float h[NS]) {
+#pragma unroll
+    for (int g = 0; g < NS / 4; ++g) {
+        const float4 f = reinterpret_cast<const float4*>(base)[g * D + d];
+        h[4 * g + 0] = f.x; h[4 * g + 1] = f.y; h[4 * g + 2] = f.z; h[4 * g + 3] = f.w;
+    }
+}
+__device__ __forceinline__ void store_state_g4(float* __restrict__ base, int64_t D, int64_t d,
+                                               const float h[NS]) {
+#pragma unroll
+    for (int g = 0; g < NS / 4; ++g)
+        reinterpret_cast<float4*>(base)[g * D + d] = make_float4(h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
+}
 __device__ __forceinline__ void store_state(float* __restrict__ p, const float h[NS]) {
     float4* q = reinterpret_cast<float4*>(p);
 #pragma unroll
@@ -265,9 +282,9 @@ __global__ __launch_bounds__(WG) void k_fwd_chunk(
         sumd += delta;
     }
     if (act) {
-        const int64_t e = ((int64_t)b * (K - 1) + k) * D + d;
-        store_state(wsS + e * NS, S);
-        wsSum[e] = sumd;
+        const int64_t e = (int64_t)b * (K - 1) + k;
+        store_state_g4(wsS + e * NS * D, D, d, S);
+        wsSum[e * D + d] = sumd;
     }
 }
 
@@ -285,12 +302,12 @@ __global__ __launch_bounds__(WG) void k_fwd_carry(
     const float* __restrict__ wsSum, float* __restrict__ starts, int D, int K,
     int64_t start_nent, int64_t start_kstep) {
     const int64_t DN = (int64_t)D * NS;
-    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;  // channel * NS + state
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;  // (state group, channel, state % 4)
     const int b = blockIdx.z;
     if (i >= DN) return;
-    const int64_t d = i / NS;
-    const float A2 = a2_of(A_log, i);
-    float h = h0 ? h0[(int64_t)b * DN + i] : 0.0f;
+    const int64_t d = (i / 4) % D, n = 4 * (i / (4 * D)) + i % 4;
+    const float A2 = a2_of(A_log, d * NS + n);
+    float h = h0 ? h0[(int64_t)b * DN + d * NS + n] : 0.0f;
     const int64_t e0 = (int64_t)b * (K - 1);  // entry of chunk 0 in wsS / wsSum
     for (int k0 = 0; k0 < K - 1; k0 += CB) {
         float Sb[CB], sb[CB];
@@ -333,7 +350,7 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
     const float Dd = Dp ? Dp[dc] : 0.0f;
     float h[NS];
     if (k > 0) {
-        load_state(starts + (((int64_t)b * start_nent + (int64_t)k * start_kstep) * D + dc) * NS, h);
+        load_state_g4(starts + ((int64_t)b * start_nent + (int64_t)k * start_kstep) * NS * D, D, dc, h);
     } else if (h0) {
         load_state(h0 + ((int64_t)b * D + dc) * NS, h);
     } else {
@@ -347,7 +364,7 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
     const T* bp = Bm + row0 * NS;
     const T* cp = Cm + row0 * NS;
     T* yp = y + row0 * D + d;
-    float* ck = ckpt ? ckpt + (((int64_t)b * nck + t0 / TS) * D + d) * NS : nullptr;
+    float* ck = ckpt ? ckpt + ((int64_t)b * nck + t0 / TS) * NS * D : nullptr;
     const int64_t ckstride = (int64_t)D * NS;
     T xq[PF], dq[PF], zq[PF];
 #pragma unroll
@@ -378,7 +395,7 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
         // load would also wait for every store issued before it
         if (i > 0 && act) yp[(int64_t)(i - 1) * D] = ypend;
         if ((i & (TS - 1)) == 0 && ck && act && (i > 0 || k == 0))
-            store_state(ck + (int64_t)(i / TS) * ckstride, h);
+            store_state_g4(ck + (int64_t)(i / TS) * ckstride, D, d, h);
         const int ip = min(i + 1, nt - 1);
         float Bv[NS], Cv[NS];
 #pragma unroll
@@ -580,7 +597,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int ts = j * TS;
         const int cnt = min(TS, t1 - ts);
         const int64_t row0 = (int64_t)b * L + ts;
-        const float* ckp = ckpt + (((int64_t)b * nck + j) * D + dc) * NS;
+        const float* ckp = ckpt + ((int64_t)b * nck + j) * NS * D;
         float hc[TS][NS];  // state after token ts+i
         // dy, z of the first RP tokens of the reverse sweep, fetched early
         constexpr int RP = 2;
@@ -593,7 +610,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
         {
             float hs[NS];
-            load_state(ckp, hs);
+            load_state_g4(ckp, D, dc, hs);
             T xr[TS], dr[TS];  // the block's x and dt, all fetched at once
 #pragma unroll
             for (int i = 0; i < TS; ++i) {
@@ -672,7 +689,13 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 const float delta = ds.x, sgu = ds.y;
                 const float dxv = delta * xv;
                 float hp[NS];
-                if (i == 0) load_state(ckp, hp);
+                if (i == 0) {
+                    // the same rows again; an opaque zero keeps the compiler from
+                    // holding the first load's addresses across the block
+                    int64_t z0 = 0;
+                    asm volatile("" : "+s"(z0));
+                    load_state_g4(ckp + z0, D, dc, hp);
+                }
                 float s1 = 0.0f, s2 = 0.0f, yacc = 0.0f;
                 float4* r4 = reinterpret_cast<float4*>(myrow);
 #pragma unroll
