@@ -727,7 +727,7 @@ def block_c_bench(args):
 # passes and reductions only add overhead on top of these.
 def kernel_alg_bytes(kernel, cfg, esz):
     ab = algorithmic_bytes(cfg, esz)
-    if kernel.startswith("k_fwd_main") or kernel.startswith("k_fwd_tile"):
+    if kernel.startswith("k_fwd_main") or kernel.startswith("k_fwd_state"):
         return ab["fwd_main"]
     if kernel.startswith("k_bwd_main") or kernel.startswith("k_bwd_tile"):
         return ab["bwd_main"]

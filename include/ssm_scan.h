@@ -121,7 +121,8 @@ enum {
     SSM_K_GDN2_WY = 18,      /* GDN2 chunked form: key side per chunk (decays, A, P, M^-1) */
     SSM_K_GDN2_STATE = 19,   /* GDN2 chunked form: state pass over the chunks (MFMA) */
     SSM_K_BLOCK_GEMM = 20,   /* one projection GEMM of the block (hipBLASLt; ssm_block.h) */
-    SSM_K_BLOCK_SUM = 21     /* fixed-order sum of a split weight gradient's partials */
+    SSM_K_BLOCK_SUM = 21,    /* fixed-order sum of a split weight gradient's partials */
+    SSM_K_FWD_STATE = 22     /* forward in one pass, one lane per (channel, state): y, checkpoints, h_last */
 };
 
 /* Name of a kernel id (for matching profiler output); "?" if unknown. */

@@ -22,6 +22,9 @@
 //     gives every chunk's true start; (3) every chunk re-runs from its start and
 //     writes y and the checkpoints.  The backward mirrors this with the adjoint
 //     (lambda <- exp(A*sum delta)*lambda + G, walking chunks in reverse).
+//   * When batch*d_inner alone gives too few lanes but 16x as many would do,
+//     the forward instead runs one lane per (channel, state) over the whole
+//     sequence in one kernel (k_fwd_state, no chunks).
 //   * The backward recomputes states from checkpoints taken every TS tokens,
 //     keeps the TS+1 states of a block in registers and sweeps it in reverse.
 //   * dB/dC (sums over channels) are reduced through LDS per wave, across the
@@ -33,6 +36,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <utility>
 
 #include "ssm_common.h"
 #include "ssm_scan.h"
@@ -53,6 +57,15 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int64_t TARGET_LANES = 262144;  // 4096 waves = 4 per SIMD
 constexpr int64_t MIN_CHUNK = 64;
+// From this many batch rows x channels up to TARGET_LANES the forward runs one
+// lane per (channel, state) over the whole sequence (k_fwd_state): at least
+// 2048 waves, 2 per SIMD.  A forward that writes checkpoints does so only below
+// STATE_LANES_CKPT_L tokens: measured at 4 x L x 5120 bf16, its checkpoint
+// stores fall behind as the sequence grows (faster than the chunked form up to
+// 14336 tokens, even at 16384, 5.1 against 4.4 ms at 32768), while without
+// checkpoints it stays ahead at every length.
+constexpr int64_t STATE_LANES_MIN = 8192;
+constexpr int64_t STATE_LANES_CKPT_L = 16384;
 constexpr int64_t NUM_CU = 256;
 // Resident workgroups of the forward main kernel (6 waves/SIMD: 73-76 VGPRs in
 // its gated variants, allocated in steps of 8 out of 512) and of the backward
@@ -300,7 +313,7 @@ __device__ __forceinline__ float a2_of(const float* __restrict__ A_log, int64_t 
 __global__ __launch_bounds__(WG) void k_fwd_carry(
     const float* __restrict__ A_log, const float* __restrict__ h0, const float* __restrict__ wsS,
     const float* __restrict__ wsSum, float* __restrict__ starts, int D, int K,
-    int64_t start_nent, int64_t start_kstep) {
+    int64_t start_bs, int64_t start_ks) {
     const int64_t DN = (int64_t)D * NS;
     const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;  // (state group, channel, state % 4)
     const int b = blockIdx.z;
@@ -321,13 +334,13 @@ __global__ __launch_bounds__(WG) void k_fwd_carry(
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
             if (k0 + j < K - 1) {
-                starts[((int64_t)b * start_nent + (int64_t)(k0 + j) * start_kstep) * DN + i] = h;
+                starts[((int64_t)b * start_bs + (int64_t)(k0 + j) * start_ks) * DN + i] = h;
                 const float P = __builtin_amdgcn_exp2f(A2 * sb[j]);
                 h = __builtin_fmaf(P, h, Sb[j]);
             }
         }
     }
-    starts[((int64_t)b * start_nent + (int64_t)(K - 1) * start_kstep) * DN + i] = h;
+    starts[((int64_t)b * start_bs + (int64_t)(K - 1) * start_ks) * DN + i] = h;
 }
 
 // (3) recurrence of chunk k from its start; writes y, checkpoints and h_last.
@@ -338,7 +351,7 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
     const float* __restrict__ Dp, const float* __restrict__ dt_bias,
     const float* __restrict__ h0, const float* __restrict__ starts, T* __restrict__ y,
     float* __restrict__ h_last, float* __restrict__ ckpt, int L, int D, int Tc, int K,
-    int64_t nck, int64_t start_nent, int64_t start_kstep) {
+    int64_t start_bs, int64_t start_ks) {
     const int d = blockIdx.x * WG + threadIdx.x;
     const int k = blockIdx.y;
     const int b = blockIdx.z;
@@ -350,7 +363,7 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
     const float Dd = Dp ? Dp[dc] : 0.0f;
     float h[NS];
     if (k > 0) {
-        load_state_g4(starts + ((int64_t)b * start_nent + (int64_t)k * start_kstep) * NS * D, D, dc, h);
+        load_state_g4(starts + ((int64_t)b * start_bs + (int64_t)k * start_ks) * NS * D, D, dc, h);
     } else if (h0) {
         load_state(h0 + ((int64_t)b * D + dc) * NS, h);
     } else {
@@ -364,8 +377,10 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
     const T* bp = Bm + row0 * NS;
     const T* cp = Cm + row0 * NS;
     T* yp = y + row0 * D + d;
-    float* ck = ckpt ? ckpt + ((int64_t)b * nck + t0 / TS) * NS * D : nullptr;
-    const int64_t ckstride = (int64_t)D * NS;
+    // checkpoints [L/8, batch, 4, D, 4]: the rows of all batch rows for one
+    // token block are adjacent
+    const int64_t ckstride = (int64_t)gridDim.z * D * NS;
+    float* ck = ckpt ? ckpt + ((int64_t)(t0 / TS) * gridDim.z + b) * NS * D : nullptr;
     T xq[PF], dq[PF], zq[PF];
 #pragma unroll
     for (int q = 0; q < PF; ++q) {
@@ -412,6 +427,217 @@ __global__ __launch_bounds__(WG) void k_fwd_main(
     }
     if (nt > 0 && act) yp[(int64_t)(nt - 1) * D] = ypend;
     if (h_last && act && k == K - 1) store_state(h_last + ((int64_t)b * D + d) * NS, h);
+}
+
+// (4) The forward in one pass, one lane per (batch, channel, state): used when
+//     batch rows x channels give too few lanes at one lane per channel, where
+//     the chunked form above would pay a second exp per element in its chunk
+//     pass.  Here every lane walks the whole sequence (16x the lanes of the
+//     chunked form, so no chunks are needed) and each element's exp is taken
+//     once.  A wave holds 4 channels x 16 states, one 16-lane row per channel.
+//     Per tile of 16 tokens:
+//       * lane n of a row does the per-token channel work (softplus, gate,
+//         output) of token t0+n and hands delta and delta*x to its row with DPP
+//         row broadcasts folded into the multiplies;
+//       * B and C of the tile are staged in LDS as [state][token] f32, so a
+//         lane reads its state's 16 values with 4 vector reads;
+//       * x, dt, z come in and y goes out through LDS as 16-channel row pieces
+//         (one instruction per tensor and tile), checkpoints as 256-byte pieces;
+//       * the readout sum over the 16 states is a butterfly over the row
+//         (the first two stages as bank-masked DPP adds); after it, lane n
+//         holds the sum of token t0+n.
+//     The states follow the same operations as scan_token(), bit for bit; the
+//     readout sums them in butterfly order instead of state order.
+constexpr int LT = 16;       // tokens per tile (= lanes per channel row)
+constexpr int LRS = LT + 4;  // LDS row stride in floats: 16-byte rows, conflict-free reads
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// one butterfly stage between lanes that differ in bit M of their row index:
+// each keeps the M slots of its half and adds the partner's copy of them
+template <int M, int CTRL>
+__device__ __forceinline__ void bfly(float* v, bool hi) {
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        const float keep = hi ? v[j + M] : v[j];
+        const float send = hi ? v[j] : v[j + M];
+        v[j] = keep + dpp_f<CTRL>(send);
+    }
+}
+template <typename F, int... I>
+__device__ __forceinline__ void for_each_i(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <typename T> struct Pair;
+template <> struct Pair<float> {
+    float2 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float2*>(p); }
+    __device__ __forceinline__ float lo() const { return v.x; }
+    __device__ __forceinline__ float hi() const { return v.y; }
+};
+template <> struct Pair<bf16_t> {
+    uint32_t v;
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint32_t*>(p); }
+    __device__ __forceinline__ float lo() const { return __uint_as_float(v << 16); }
+    __device__ __forceinline__ float hi() const { return __uint_as_float(v & 0xffff0000u); }
+};
+
+// 4 consecutive activations of one token row (8 bytes in bf16, 16 in f32)
+template <typename T> struct Quad;
+template <> struct Quad<float> {
+    float4 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ void store(float* p) const { *reinterpret_cast<float4*>(p) = v; }
+};
+template <> struct Quad<bf16_t> {
+    uint2 v;
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ void store(bf16_t* p) const { *reinterpret_cast<uint2*>(p) = v; }
+};
+
+template <typename T, bool GATE, bool CK>
+__global__ __launch_bounds__(WG) void k_fwd_state(
+    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
+    const T* __restrict__ Cm, const T* __restrict__ z, const float* __restrict__ A_log,
+    const float* __restrict__ Dp, const float* __restrict__ dt_bias,
+    const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_last,
+    float* __restrict__ ckpt, int L, int D, int ncb) {
+    __shared__ float bc[2][2][NS * LRS];    // [buffer][B, C][state][token]
+    __shared__ T act_s[2][3][LT][16];       // [buffer][x, dt, z][token][channel of the block]
+    __shared__ T y_s[2][LT][16];            // [buffer][token][channel of the block]
+    __shared__ float4 ck_s[2][2][4][16];     // [buffer][checkpoint][state group][channel of the block]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15;
+    // channel blocks of 16; the 4 blocks of one 64-channel row segment are
+    // numbered onto one XCD (blocks are dealt to the 8 XCDs round robin)
+    const int xb = blockIdx.x;
+    const int cb = 4 * ((xb & 7) + 8 * (xb >> 5)) + ((xb >> 3) & 3);
+    if (cb >= ncb) return;  // uniform over the workgroup
+    const int cw = wave * 4 + (lane >> 4);  // channel within the block
+    const int d = cb * 16 + cw;             // D is a multiple of 16 on this path
+    const int b = blockIdx.y;
+    const float A2 = a2_of(A_log, (int64_t)d * NS + n);
+    const float bias = dt_bias ? dt_bias[d] : 0.0f;
+    const float Dd = Dp ? Dp[d] : 0.0f;
+    float h = h0 ? h0[((int64_t)b * D + d) * NS + n] : 0.0f;
+    const int64_t row0 = (int64_t)b * L;
+    // B and C staging: thread -> (tensor, token, pair of states)
+    const int st = threadIdx.x >> 7, sw = threadIdx.x & 127, stok = sw >> 3, sn = 2 * (sw & 7);
+    const T* sp = (st ? Cm : Bm) + row0 * NS + sn;
+    // activation staging (threads 0..191) and output rows (threads 0..63):
+    // thread -> (tensor, token, 4 channels)
+    const int aq = threadIdx.x >> 6, atok = (threadIdx.x & 63) >> 2, a4 = 4 * (threadIdx.x & 3);
+    const bool astage = threadIdx.x < 3 * 64 && (GATE || aq < 2);
+    const T* ap = (aq == 0 ? x : aq == 1 ? dt : z) + row0 * D + cb * 16 + a4;
+    T* yrow = y + row0 * D + cb * 16 + a4;
+    const int ntile = (L + LT - 1) / LT;
+    // checkpoints of the previous tile (states before its tokens 0 and 8),
+    // written as 4 x 256-byte pieces per checkpoint: thread -> (checkpoint,
+    // state group, channel)
+    auto store_ck = [&](int buf, int tp) {
+        const int which = threadIdx.x >> 6, g = (threadIdx.x >> 4) & 3, c16 = threadIdx.x & 15;
+        if (CK && threadIdx.x < 128 && tp + TS * which < L) {
+            const int64_t j = (tp + TS * which) / TS;
+            reinterpret_cast<float4*>(ckpt)[((j * gridDim.y + b) * 4 + g) * D + cb * 16 + c16] =
+                ck_s[buf][which][g][c16];
+        }
+    };
+    float* ckl = reinterpret_cast<float*>(&ck_s[0][0][n >> 2][cw]) + (n & 3);
+    constexpr int CKBUF = 2 * 4 * 16 * 4;  // floats per buffer
+    auto stage_load = [&](int t1, Pair<T>& pbc, Quad<T>& pa) {
+        pbc.load(sp + (int64_t)min(t1 + stok, L - 1) * NS);
+        if (astage) pa.load(ap + (int64_t)min(t1 + atok, L - 1) * D);
+    };
+    auto stage_store = [&](int buf, const Pair<T>& pbc, const Quad<T>& pa) {
+        bc[buf][st][sn * LRS + stok] = pbc.lo();
+        bc[buf][st][(sn + 1) * LRS + stok] = pbc.hi();
+        if (astage) pa.store(&act_s[buf][aq][atok][a4]);
+    };
+    // rows of the previous tile's outputs, one 4-channel piece per thread
+    auto store_y = [&](int buf, int tp) {
+        if (threadIdx.x < 64 && tp + atok < L) {
+            Quad<T> q;
+            q.load(&y_s[buf][atok][a4]);
+            q.store(yrow + (int64_t)(tp + atok) * D);
+        }
+    };
+    {
+        Pair<T> p0;
+        Quad<T> a0;
+        stage_load(0, p0, a0);
+        stage_store(0, p0, a0);
+    }
+    __syncthreads();
+    auto tile = [&](int k, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        const int t0 = k * LT;
+        const int buf = k & 1;
+        Pair<T> pbc;
+        Quad<T> pa;
+        stage_load(t0 + LT, pbc, pa);  // the next tile's loads first
+        __builtin_amdgcn_sched_barrier(0);
+        float Bv[LT], Cv[LT];
+        {
+            const float4* pb = reinterpret_cast<const float4*>(&bc[buf][0][n * LRS]);
+            const float4* pc = reinterpret_cast<const float4*>(&bc[buf][1][n * LRS]);
+#pragma unroll
+            for (int q = 0; q < LT / 4; ++q) {
+                const float4 fb = pb[q], fc = pc[q];
+                Bv[4 * q + 0] = fb.x; Bv[4 * q + 1] = fb.y; Bv[4 * q + 2] = fb.z; Bv[4 * q + 3] = fb.w;
+                Cv[4 * q + 0] = fc.x; Cv[4 * q + 1] = fc.y; Cv[4 * q + 2] = fc.z; Cv[4 * q + 3] = fc.w;
+            }
+        }
+        // this lane's token of the tile
+        const float xv = to_f(act_s[buf][0][n][cw]);
+        const float zv = GATE ? to_f(act_s[buf][2][n][cw]) : 0.0f;
+        float sg;
+        const float delta = softplus_sig(to_f(act_s[buf][1][n][cw]) + bias, sg);
+        const float dxv = delta * xv;
+        if (k > 0) {
+            store_y(buf ^ 1, t0 - LT);
+            store_ck(buf ^ 1, t0 - LT);
+        }
+        float yp[LT];
+        for_each_i([&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            if (FULL || t0 + I < L) {
+                if (CK && (I % TS) == 0)  // state before token t0+I
+                    ckl[buf * CKBUF + (I / TS) * 4 * 16 * 4] = h;
+                const float a = __builtin_amdgcn_exp2f(dpp_f<0x150 + I>(delta) * A2);
+                h = __builtin_fmaf(a, h, dpp_f<0x150 + I>(dxv) * Bv[I]);
+                yp[I] = Cv[I] * h;
+            } else {
+                yp[I] = 0.0f;
+            }
+        }, std::make_integer_sequence<int, LT>{});
+        {
+            float o8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+                    "v_add_f32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xc"
+                    : "=&v"(o8[j]) : "v"(yp[j]), "v"(yp[j + 8]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+                    "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
+                    : "=&v"(yp[j]) : "v"(o8[j]), "v"(o8[j + 4]));
+        }
+        bfly<2, 0x4E>(yp, (n & 2) != 0);   // quad_perm [2,3,0,1]
+        bfly<1, 0xB1>(yp, (n & 1) != 0);   // quad_perm [1,0,3,2]
+        y_s[buf][n][cw] = from_f<T>(finish_y<GATE>(yp[0], Dd, xv, zv));
+        __builtin_amdgcn_sched_barrier(0);  // the loads are first used here, a tile after their issue
+        stage_store(buf ^ 1, pbc, pa);
+        __syncthreads();
+    };
+    const int nfull = L / LT;
+    for (int k = 0; k < nfull; ++k) tile(k, std::true_type{});
+    if (nfull < ntile) tile(nfull, std::false_type{});
+    store_y((ntile - 1) & 1, (ntile - 1) * LT);
+    store_ck((ntile - 1) & 1, (ntile - 1) * LT);
+    if (h_last) h_last[((int64_t)b * D + d) * NS + n] = h;
 }
 
 // ==================================================================== backward
@@ -545,7 +771,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const float* __restrict__ Xin, T* __restrict__ dxo, T* __restrict__ ddto,
     T* __restrict__ dzo, float* __restrict__ dh0, float* __restrict__ wsBC,
     float* __restrict__ wsPA, float* __restrict__ wsPD, int L, int D, int Tc, int K,
-    int64_t nck, int ndb) {
+    int ndb) {
     constexpr int RS = 36;  // LDS row stride in floats: 16-byte aligned rows
     static_assert(TS * 32 <= WG, "one dB/dC partial per thread at the block end");
     __shared__ float rows[NWAVE][64 * RS];
@@ -597,7 +823,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int ts = j * TS;
         const int cnt = min(TS, t1 - ts);
         const int64_t row0 = (int64_t)b * L + ts;
-        const float* ckp = ckpt + ((int64_t)b * nck + j) * NS * D;
+        const float* ckp = ckpt + ((int64_t)j * gridDim.z + b) * NS * D;
         float hc[TS][NS];  // state after token ts+i
         // dy, z of the first RP tokens of the reverse sweep, fetched early
         constexpr int RP = 2;
@@ -630,7 +856,6 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
             for (int i = 0; i < TS; ++i) {
                 if (i < cnt) {
-                    const int64_t row = row0 + i;
                     const float xv = to_f(xr[i]), dtv = to_f(dr[i]);
                     float Bv[NS];
                     bn.get(Bv);
@@ -968,6 +1193,8 @@ struct Plan {
     int64_t Tf, Kf;  // forward chunk length / count
     int64_t Tb, Kb;  // backward chunk length / count
     int64_t nck, ndb;
+    bool state_lanes;       // forward without checkpoints by k_fwd_state (one lane per channel and state)
+    bool state_lanes_ckpt;  // the same with checkpoints (then Kf = 1: no forward workspace)
 };
 
 ssm_status check_dims(const ssm_dims* d) {
@@ -1023,7 +1250,10 @@ Plan make_plan(const ssm_dims* d) {
     // Forward: one chunk (a purely sequential scan, same operation order as the
     // single-token step) when the channels alone fill the chip or the sequence
     // is short.
-    if (p.Bt * p.D >= TARGET_LANES || p.L < 2 * MIN_CHUNK) p.Tf = (Lp + TS - 1) / TS * TS;
+    p.state_lanes = p.Bt * p.D >= STATE_LANES_MIN && p.Bt * p.D < TARGET_LANES && p.Bt <= 65535 &&
+                    p.D % 16 == 0;
+    p.state_lanes_ckpt = p.state_lanes && p.L < STATE_LANES_CKPT_L;
+    if (p.state_lanes_ckpt || p.Bt * p.D >= TARGET_LANES || p.L < 2 * MIN_CHUNK) p.Tf = (Lp + TS - 1) / TS * TS;
     else p.Tf = pick_chunk(p.L, p.Bt * p.ndb, FWD_SLOTS);
     p.Kf = (Lp + p.Tf - 1) / p.Tf;
     p.Tb = p.L < 2 * MIN_CHUNK ? (Lp + TS - 1) / TS * TS : pick_chunk(p.L, p.Bt * p.ndb, BWD_SLOTS);
@@ -1084,27 +1314,37 @@ ssm_status run_fwd(const Plan& p, const void* x, const void* dt, const void* B, 
     float* S = p.Kf > 1 ? reinterpret_cast<float*>(wsb + w.S) : nullptr;
     float* sum = p.Kf > 1 ? reinterpret_cast<float*>(wsb + w.sum) : nullptr;
     float* starts;
-    int64_t nent, kstep;
-    if (ckpt) {
+    int64_t sb, sk;  // entry of chunk k of batch row b: b * sb + k * sk
+    if (ckpt) {          // chunk starts are checkpoints: [L/8, batch, ...]
         starts = ckpt;
-        nent = p.nck;
-        kstep = p.Tf / TS;
+        sb = 1;
+        sk = p.Tf / TS * p.Bt;
     } else {
         starts = p.Kf > 1 ? reinterpret_cast<float*>(wsb + w.starts) : nullptr;
-        nent = p.Kf;
-        kstep = 1;
+        sb = p.Kf;
+        sk = 1;
     }
     const int L = (int)p.L, D = (int)p.D, Tc = (int)p.Tf, K = (int)p.Kf;
+    if (ckpt ? p.state_lanes_ckpt : p.state_lanes) {
+        const int ncb = D / 16;
+        const dim3 grid((unsigned)((ncb + 31) / 32 * 32), (unsigned)p.Bt);
+        if (ckpt)
+            return launch(SSM_K_FWD_STATE, k_fwd_state<T, GATE, true>, grid, (const T*)x, (const T*)dt,
+                          (const T*)B, (const T*)C, (const T*)z, A_log, Dp, dt_bias, h0, (T*)y, h_last,
+                          ckpt, L, D, ncb);
+        return launch(SSM_K_FWD_STATE, k_fwd_state<T, GATE, false>, grid, (const T*)x, (const T*)dt,
+                      (const T*)B, (const T*)C, (const T*)z, A_log, Dp, dt_bias, h0, (T*)y, h_last, ckpt,
+                      L, D, ncb);
+    }
     if (p.Kf > 1) {
         SSM_TRY(launch(SSM_K_FWD_CHUNK, k_fwd_chunk<T>, dim3(p.ndb, p.Kf - 1, p.Bt),
                        (const T*)x, (const T*)dt, (const T*)B, A_log, dt_bias, S, sum, L, D, Tc, K));
         SSM_TRY(launch(SSM_K_FWD_CARRY, k_fwd_carry, dim3((unsigned)((p.D * NS + WG - 1) / WG), 1, p.Bt), A_log, h0,
-                       (const float*)S, (const float*)sum, starts, D, K, nent, kstep));
+                       (const float*)S, (const float*)sum, starts, D, K, sb, sk));
     }
     return launch(SSM_K_FWD_MAIN, k_fwd_main<T, GATE>, dim3(p.ndb, p.Kf, p.Bt), (const T*)x,
                   (const T*)dt, (const T*)B, (const T*)C, (const T*)z, A_log, Dp, dt_bias, h0,
-                  (const float*)starts, (T*)y, h_last, ckpt, L, D, Tc, K, (int64_t)p.nck, nent,
-                  kstep);
+                  (const float*)starts, (T*)y, h_last, ckpt, L, D, Tc, K, sb, sk);
 }
 
 template <typename T, bool GATE>
@@ -1132,7 +1372,7 @@ ssm_status run_bwd(const Plan& p, const void* x, const void* dt, const void* B, 
     SSM_TRY(launch(SSM_K_BWD_MAIN, k_bwd_main<T, GATE>, dim3(p.ndb, p.Kb, p.Bt), (const T*)x,
                    (const T*)dt, (const T*)B, (const T*)C, (const T*)z, (const T*)dy, A_log, Dp,
                    dt_bias, ckpt, (const float*)X, (T*)dx, (T*)ddt, (T*)dz, dh0, BC, PA, PD, L,
-                   D, Tc, K, (int64_t)p.nck, (int)p.ndb));
+                   D, Tc, K, (int)p.ndb));
     const int64_t rows = p.Bt * p.L;
     SSM_TRY(launch(SSM_K_BWD_REDUCE_BC, k_bwd_reduce_bc<T>, dim3((unsigned)((rows * 32 + WG - 1) / WG)),
                    (const float*)BC, (T*)dB, (T*)dC, rows, (int)p.ndb));
@@ -1168,6 +1408,7 @@ const char* ssm_kernel_name(int32_t id) {
         case SSM_K_FWD_CHUNK: return "k_fwd_chunk";
         case SSM_K_FWD_CARRY: return "k_fwd_carry";
         case SSM_K_FWD_MAIN: return "k_fwd_main";
+        case SSM_K_FWD_STATE: return "k_fwd_state";
         case SSM_K_BWD_CHUNK: return "k_bwd_chunk";
         case SSM_K_BWD_CARRY: return "k_bwd_carry";
         case SSM_K_BWD_MAIN: return "k_bwd_main";

@@ -37,7 +37,7 @@ int main() {
         if (!ssm_kernel_name(k)) ++fails;
 
     // ---- scan: size queries
-    ssm_dims ok{2, 64, 32, 16, SSM_F32}, big{8, 2048, 1536, 16, SSM_F32};
+    ssm_dims ok{2, 64, 32, 16, SSM_F32}, big{2, 4096, 1536, 16, SSM_F32};  // big: a chunked forward
     ssm_dims bad[] = {{0, 64, 32, 16, SSM_F32}, {2, -1, 32, 16, SSM_F32}, {2, 64, 0, 16, SSM_F32},
                       {2, 64, 32, 8, SSM_F32},  {2, 64, 32, 16, 7},         {70000, 64, 32, 16, SSM_F32}};
     if (ssm_scan_ckpt_bytes(&ok) == 0 || ssm_scan_bwd_workspace_bytes(&ok) == 0) ++fails;

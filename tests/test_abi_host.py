@@ -47,8 +47,8 @@ def test_block_header_exports_present():
 
 
 def test_kernel_names():
-    names = [ssm.kernel_name(i) for i in range(1, 18)]
-    assert "?" not in names and len(set(names)) == 17
+    names = [ssm.kernel_name(i) for i in range(1, 23)]
+    assert "?" not in names and len(set(names)) == 22
     assert ssm.kernel_name(99) == "?"
 
 
@@ -70,8 +70,10 @@ def test_query_sizes():
     for bad in (_dims(0), _dims(L=-1), _dims(d=0), _dims(n=8), _dims(io=5)):
         assert lib.ssm_scan_ckpt_bytes(ctypes.byref(bad)) == 0
         assert lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(bad)) == 0
-    big = _dims(8, 2048, 1536)
+    big = _dims(2, 4096, 1536)
     assert lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(big)) > 0       # chunked sequence
+    lanes = _dims(8, 2048, 1536)
+    assert lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(lanes)) == 0     # one lane per state, no chunks
 
 
 FAKE = 1 << 20  # 16-byte aligned non-null fake device address: never dereferenced
@@ -100,7 +102,7 @@ def test_fwd_rejects_bad_arguments():
     assert _fwd(_dims(), y=None) == NULLPTR
     assert _fwd(_dims(), dt=FAKE + 4) == ALIGN
     assert _fwd(_dims(), z=FAKE + 2) == ALIGN
-    big = _dims(8, 2048, 1536)
+    big = _dims(2, 4096, 1536)  # chunked: needs a workspace
     need = lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(big))
     assert _fwd(big) == WORKSPACE
     assert _fwd(big, ws=FAKE, ws_bytes=need - 1) == WORKSPACE

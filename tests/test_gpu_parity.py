@@ -11,7 +11,8 @@ Covers the five workloads (tiny f32, Mamba-130M-shaped f32 fwd and fwd+bwd,
 Mamba-2.8B-shaped bf16 fwd+bwd, 1024 decode steps) and guard shapes: long
 memory (128 chunks), random A_log, ragged lengths/channels, split invariance,
 determinism, delta -> 0, delta = 100, constant inputs, no gate / no D / no
-bias / h0 / dh0, seqlen 0.
+bias / h0 / dh0, seqlen 0, and the one-lane-per-state forward used at widths
+of 8192 to 262143 batch rows x channels.
 """
 import numpy as np
 import pytest
@@ -388,6 +389,85 @@ def test_step_row_groups_match_forward(io, gate):
     torch.cuda.synchronize()
     assert torch.equal(torch.stack(ys, 1), y)
     assert torch.equal(hs, h)
+
+
+# Widths from 8192 up to 262143 batch rows x channels (d_inner a multiple of 16)
+# run the forward with one lane per (channel, state) over the whole sequence
+# (k_fwd_state, no chunks, no forward workspace); 2 x 4096 below.
+@pytest.mark.parametrize("L", [1, 17, 1000])
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("gate", [True, False])
+def test_state_lane_forward(L, io, gate):
+    """One-token and ragged sequences (17 = one 16-token tile and one token,
+    1000 = 62 tiles and 8 tokens), with h0; with the gate, D and dt_bias, or
+    with none of them.  The backward reads the checkpoints this forward writes."""
+    assert ssm.fwd_workspace_bytes(2, L, 4096, io_dtype=io) == 0
+    inp = W.make_inputs(2, L, 4096, seed=31 + L, bf16=io == torch.bfloat16)
+    if not gate:
+        inp["z"] = None
+        inp["D"] = None
+        inp["dt_bias"] = None
+    h0 = (0.5 * np.random.default_rng(7).standard_normal((2, 4096, 16))).astype(np.float32)
+    tol = (F32_FWD, F32_GRAD) if io == torch.float32 else (BF16_TOL, BF16_TOL)
+    _check_all(inp, io=io, h0=h0, fwd_tol=tol[0], grad_tol=tol[1], want_dh0=True)
+
+
+def test_state_lane_inference_equals_training_forward():
+    """Without checkpoints (inference) the same kernel computes the same bits."""
+    inp = W.make_inputs(2, 300, 4096, seed=41, with_dy=False)
+    t = {k: _t(v) for k, v in inp.items()}
+    args = (t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"])
+    y1, h1, ck = ssm.ssm_scan_fwd(*args, training=True, return_last_state=True)
+    y2, h2, _ = ssm.ssm_scan_fwd(*args, training=False, return_last_state=True)
+    torch.cuda.synchronize()
+    assert ck is not None
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_state_lane_states_match_step_chain():
+    """Each state goes through the same operations as in the single-token step:
+    after 40 tokens the states agree bit for bit.  The readout sums the 16
+    states in butterfly order rather than state order, so y agrees to
+    rounding."""
+    inp = W.make_inputs(2, 40, 4096, seed=43, with_dy=False)
+    t = {k: _t(v) for k, v in inp.items()}
+    y, h, _ = ssm.ssm_scan_fwd(t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"],
+                               return_last_state=True)
+    hs = torch.zeros(2, 4096, 16, device=DEV)
+    ys = []
+    for s_ in range(40):
+        sl = {k: t[k][:, s_].contiguous() for k in ("x", "dt", "B", "C", "z")}
+        ys.append(ssm.ssm_scan_step(hs, sl["x"], sl["dt"], sl["B"], sl["C"], sl["z"], t["A_log"], t["D"],
+                                    t["dt_bias"]))
+    torch.cuda.synchronize()
+    assert torch.equal(hs, h)
+    assert _rel(torch.stack(ys, 1), _np(y)) <= 1e-6
+
+
+def test_state_lane_bf16_is_nearest_even_of_f32():
+    """bf16 I/O on the lane-per-state forward: the stored y is the nearest-even
+    rounding of the f32-I/O result, bit for bit."""
+    inp = W.make_inputs(2, 100, 4096, seed=44, bf16=True, with_dy=False)
+    y32, _, _ = _gpu_fwd_bwd(inp, io=torch.float32, bwd=False)
+    y16, _, _ = _gpu_fwd_bwd(inp, io=torch.bfloat16, bwd=False)
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+
+
+def test_long_sequence_forwards_agree():
+    """From 16384 tokens a forward that writes checkpoints takes the chunked form
+    (the lane-per-state forward's checkpoint stores fall behind there), while
+    inference keeps one lane per state: both must give the same y and h_last to
+    rounding (they sum in different orders)."""
+    assert ssm.fwd_workspace_bytes(1, 16400, 8192) > 0  # training: chunked
+    inp = W.make_inputs(1, 16400, 8192, seed=45, with_dy=False, dt_bias=W.DT_BIAS_SLOW)
+    t = {k: _t(v) for k, v in inp.items()}
+    args = (t["x"], t["dt"], t["B"], t["C"], t["z"], t["A_log"], t["D"], t["dt_bias"])
+    y_tr, h_tr, ck = ssm.ssm_scan_fwd(*args, training=True, return_last_state=True)
+    y_in, h_in, _ = ssm.ssm_scan_fwd(*args, training=False, return_last_state=True)
+    torch.cuda.synchronize()
+    assert ck is not None
+    assert _rel(y_in, _np(y_tr)) <= 1e-5
+    assert _rel(h_in, _np(h_tr)) <= 1e-5
 
 
 def test_bf16_outputs_are_nearest_even_roundings_of_the_f32_path():
