@@ -470,6 +470,7 @@ template <typename F, int... I>
 __device__ __forceinline__ void for_each_i(F&& f, std::integer_sequence<int, I...>) {
     (f(std::integral_constant<int, I>{}), ...);
 }
+// two consecutive states' values of one B or C row (4 bytes in bf16, 8 in f32)
 template <typename T> struct Pair;
 template <> struct Pair<float> {
     float2 v;
@@ -612,6 +613,13 @@ __global__ __launch_bounds__(WG) void k_fwd_state(
                 yp[I] = 0.0f;
             }
         }, std::make_integer_sequence<int, LT>{});
+        // readout: butterfly over the row's 16 lanes.  Stage 1 pairs lane i with
+        // i^8 (row_ror:8): lanes 0-7 (banks 0,1) keep tokens 0-7, lanes 8-15
+        // (banks 2,3) tokens 8-15, each adding the partner's copy; stage 2 does
+        // the same within each half with row_half_mirror (lane i with 7-i; banks
+        // 0,2 keep the lower 4 slots).  A bank-masked DPP add writes only its
+        // banks, so each stage is 2 instructions per pair, no selects.  The
+        // s_nop covers the DPP read-after-VALU-write hazard inside the asm.
         {
             float o8[8];
 #pragma unroll
