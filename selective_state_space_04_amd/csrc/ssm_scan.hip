@@ -23,8 +23,9 @@
 //     writes y and the checkpoints.  The backward mirrors this with the adjoint
 //     (lambda <- exp(A*sum delta)*lambda + G, walking chunks in reverse).
 //   * When batch*d_inner alone gives too few lanes but 16x as many would do,
-//     the forward instead runs one lane per (channel, state) over the whole
-//     sequence in one kernel (k_fwd_state, no chunks).
+//     or the sequence is short, the forward instead runs one lane per
+//     (channel, state) over the whole sequence in one kernel (k_fwd_state, no
+//     chunks).
 //   * The backward recomputes states from checkpoints taken every TS tokens,
 //     keeps the TS+1 states of a block in registers and sweeps it in reverse.
 //   * dB/dC (sums over channels) are reduced through LDS per wave, across the
@@ -66,6 +67,9 @@ constexpr int64_t MIN_CHUNK = 64;
 // checkpoints it stays ahead at every length.
 constexpr int64_t STATE_LANES_MIN = 8192;
 constexpr int64_t STATE_LANES_CKPT_L = 16384;
+// Below STATE_LANES_MIN the lane-per-state forward is still taken for sequences of
+// up to this many tokens, where the chunked form is bound by latency.
+constexpr int64_t STATE_LANES_SHORT_L = 512;
 constexpr int64_t NUM_CU = 256;
 // Resident workgroups of the forward main kernel (6 waves/SIMD: 73-76 VGPRs in
 // its gated variants, allocated in steps of 8 out of 512) and of the backward
@@ -1222,8 +1226,9 @@ ssm_status check_dims(const ssm_dims* d) {
 // fills whole rounds of resident workgroups best (the last round of a launch
 // otherwise runs partly empty), among counts that fill the chip at least once;
 // ties go to fewer chunks.  Tiny problems take as many chunks as allowed.
-int64_t pick_chunk(int64_t L, int64_t wg_per_chunk, int64_t slots) {
-    const int64_t kmax = std::max<int64_t>(1, std::min<int64_t>(L / MIN_CHUNK, 4096));
+int64_t pick_chunk(int64_t L, int64_t wg_per_chunk, int64_t slots, int64_t min_chunk = MIN_CHUNK) {
+    if (L < 1) return TS;  // empty sequence: one (empty) chunk
+    const int64_t kmax = std::max<int64_t>(1, std::min<int64_t>(L / min_chunk, 4096));
     int64_t best_tc = -1;
     double best_eff = -1.0;
     int64_t prev_k = -1;
@@ -1255,16 +1260,22 @@ Plan make_plan(const ssm_dims* d) {
     p.nck = (p.L + TS - 1) / TS;
     p.ndb = (p.D + WG - 1) / WG;
     const int64_t Lp = std::max<int64_t>(p.L, 1);
-    // Forward: one chunk (a purely sequential scan, same operation order as the
+    // Forward: one lane per state (k_fwd_state) at the widths and lengths above;
+    // else one chunk (a purely sequential scan, same operation order as the
     // single-token step) when the channels alone fill the chip or the sequence
-    // is short.
-    p.state_lanes = p.Bt * p.D >= STATE_LANES_MIN && p.Bt * p.D < TARGET_LANES && p.Bt <= 65535 &&
-                    p.D % 16 == 0;
+    // is short; else chunks.  Backward: chunks sized to fill the resident slots;
+    // with few workgroups per chunk, chunks down to one 8-token block, so that
+    // short sequences are not walked by a handful of waves one token at a time.
+    p.state_lanes = p.Bt * p.D < TARGET_LANES && p.Bt <= 65535 && p.D % 16 == 0 &&
+                    (p.Bt * p.D >= STATE_LANES_MIN || p.L <= STATE_LANES_SHORT_L);
     p.state_lanes_ckpt = p.state_lanes && p.L < STATE_LANES_CKPT_L;
     if (p.state_lanes_ckpt || p.Bt * p.D >= TARGET_LANES || p.L < 2 * MIN_CHUNK) p.Tf = (Lp + TS - 1) / TS * TS;
     else p.Tf = pick_chunk(p.L, p.Bt * p.ndb, FWD_SLOTS);
     p.Kf = (Lp + p.Tf - 1) / p.Tf;
-    p.Tb = p.L < 2 * MIN_CHUNK ? (Lp + TS - 1) / TS * TS : pick_chunk(p.L, p.Bt * p.ndb, BWD_SLOTS);
+    if (p.Bt * p.ndb * 8 <= BWD_SLOTS && p.L >= 2 * TS)  // few workgroups per chunk: chunks down to 8 tokens
+        p.Tb = pick_chunk(p.L, p.Bt * p.ndb, BWD_SLOTS, TS);
+    else
+        p.Tb = p.L < 2 * MIN_CHUNK ? (Lp + TS - 1) / TS * TS : pick_chunk(p.L, p.Bt * p.ndb, BWD_SLOTS);
     p.Kb = (Lp + p.Tb - 1) / p.Tb;
     return p;
 }

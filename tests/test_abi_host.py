@@ -76,6 +76,19 @@ def test_query_sizes():
     assert lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(lanes)) == 0     # one lane per state, no chunks
 
 
+def test_size_queries_on_valid_dims_of_every_planner_regime():
+    """The chunk planner runs on every valid shape: empty, one-token and short
+    sequences, widths below and above each regime's bounds.  A planner bug such
+    as a zero chunk length for an empty sequence would end the process here."""
+    for b in (1, 2, 3, 64, 300):
+        for L in (0, 1, 2, 7, 8, 9, 15, 16, 17, 63, 64, 65, 127, 128, 129, 511, 512, 513, 4096, 16384):
+            for d in (1, 16, 33, 256, 1536, 5120):
+                dm = _dims(b, L, d)
+                lib.ssm_scan_fwd_workspace_bytes(ctypes.byref(dm))
+                lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(dm))
+                assert lib.ssm_scan_ckpt_bytes(ctypes.byref(dm)) == 4 * b * ((L + 7) // 8) * d * 16
+
+
 FAKE = 1 << 20  # 16-byte aligned non-null fake device address: never dereferenced
 
 
