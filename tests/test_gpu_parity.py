@@ -453,6 +453,17 @@ def test_state_lane_bf16_is_nearest_even_of_f32():
     assert torch.equal(y16, y32.to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("L", [3, 17])
+def test_state_lane_forward_many_batch_rows(L):
+    """16383 batch rows x 16 channels (262128 lanes' worth, the widest the
+    lane-per-state forward takes): a grid of 16383 rows of workgroups, one
+    16-channel block each, with whole and partial tiles; the backward reads the
+    checkpoints they write."""
+    inp = W.make_inputs(16383, L, 16, seed=46 + L)
+    assert ssm.fwd_workspace_bytes(16383, L, 16) == 0
+    _check_all(inp, want_dh0=True)
+
+
 def test_long_sequence_forwards_agree():
     """From 16384 tokens a forward that writes checkpoints takes the chunked form
     (the lane-per-state forward's checkpoint stores fall behind there), while
