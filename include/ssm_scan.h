@@ -187,9 +187,13 @@ ssm_status ssm_scan_bwd(const ssm_dims *dims, const void *x, const void *dt, con
 
 /* Single-token step (commit introducing MambaRecurrence::step): the forward's
  * per-token body applied to a caller-held state, updated in place.  Stepping
- * token by token from a zero state equals ssm_scan_fwd bit for bit whenever
- * the forward runs its sequence in one chunk (it does so whenever
- * batch*d_inner >= 262144 or seqlen < 128).
+ * token by token from a zero state equals ssm_scan_fwd bit for bit (states and
+ * y) whenever the forward runs its sequence as one chunk with one lane per
+ * channel: when batch*d_inner >= 262144, or seqlen < 128 and d_inner is not a
+ * multiple of 16.  Where the forward runs one lane per state instead
+ * (batch*d_inner < 262144, d_inner a multiple of 16, and batch*d_inner >= 8192
+ * or seqlen <= 512) the states still agree bit for bit and y to rounding: its
+ * readout sums the 16 states in another order.
  *   h          : [batch, d_inner, N] f32, read and overwritten
  *   x, dt, z   : [batch, d_inner] io dtype (z nullable)
  *   B, C       : [batch, N] io dtype
