@@ -18,8 +18,12 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def _scan_inputs(io=torch.bfloat16):
-    inp = W.make_inputs(2, 1000, 384, seed=61, bf16=io == torch.bfloat16)
+# (2, 1000, 384): the chunked forward; (2, 1000, 4096): one lane per state
+SCAN_SHAPES = [(2, 1000, 384), (2, 1000, 4096)]
+
+
+def _scan_inputs(io=torch.bfloat16, shape=SCAN_SHAPES[0]):
+    inp = W.make_inputs(*shape, seed=61, bf16=io == torch.bfloat16)
     return {k: torch.from_numpy(v).to(DEV).to(io if k in ("x", "z", "dt", "B", "C", "dy") else torch.float32)
             for k, v in inp.items() if v is not None}
 
@@ -41,8 +45,9 @@ def _same(a, b):
     return all(torch.equal(a[k], b[k]) for k in a if a[k] is not None)
 
 
-def test_scan_on_a_side_stream_matches_default_stream():
-    t = _scan_inputs()
+@pytest.mark.parametrize("shape", SCAN_SHAPES)
+def test_scan_on_a_side_stream_matches_default_stream(shape):
+    t = _scan_inputs(shape=shape)
     y0, g0 = torch.empty_like(t["x"]), _fresh_grads(t)
     _scan_step(t, y0, g0)
     torch.cuda.synchronize()
@@ -55,13 +60,14 @@ def test_scan_on_a_side_stream_matches_default_stream():
     assert torch.equal(y0, y1) and _same(g0, g1)
 
 
-def test_explicit_stream_without_entering_its_context():
+@pytest.mark.parametrize("shape", SCAN_SHAPES)
+def test_explicit_stream_without_entering_its_context(shape):
     """stream= passed while another stream is current: the workspace, checkpoints
     and outputs the binding allocates must belong to the launch stream, so that
     allocations made meanwhile on the current stream cannot reuse them while the
     kernels still run.  Busy work on the side stream keeps the kernels in flight
     while the current stream allocates and fills fresh memory."""
-    t = _scan_inputs()
+    t = _scan_inputs(shape=shape)
     y0, g0 = torch.empty_like(t["x"]), _fresh_grads(t)
     _scan_step(t, y0, g0)
     torch.cuda.synchronize()
@@ -82,8 +88,9 @@ def test_explicit_stream_without_entering_its_context():
     assert torch.equal(y0, y1) and _same(g0, g1)
 
 
-def test_scan_fwd_bwd_graph_replays_equal_eager():
-    t = _scan_inputs()
+@pytest.mark.parametrize("shape", SCAN_SHAPES)
+def test_scan_fwd_bwd_graph_replays_equal_eager(shape):
+    t = _scan_inputs(shape=shape)
     y_ref, g_ref = torch.empty_like(t["x"]), _fresh_grads(t)
     _scan_step(t, y_ref, g_ref)
     torch.cuda.synchronize()

@@ -66,7 +66,8 @@ def _run(t, io, byte):
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("shape,bias", [((1, 64, 32), W.DT_BIAS_ACTIVE),      # one chunk
                                         ((2, 1000, 100), W.DT_BIAS_SLOW),    # chunks with ragged ends
-                                        ((3, 777, 300), W.DT_BIAS_ACTIVE)])  # 2 channel blocks, partial
+                                        ((3, 777, 300), W.DT_BIAS_ACTIVE),   # 2 channel blocks, partial
+                                        ((2, 300, 4096), W.DT_BIAS_ACTIVE)])  # one lane per state
 def test_outputs_do_not_depend_on_prior_buffer_contents(shape, bias, io):
     inp = W.make_inputs(*shape, seed=21, dt_bias=bias, bf16=io == torch.bfloat16)
     t = {k: (None if v is None else torch.from_numpy(v).to(DEV)) for k, v in inp.items()}
