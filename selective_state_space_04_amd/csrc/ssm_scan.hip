@@ -555,6 +555,19 @@ __global__ __launch_bounds__(WG) void k_fwd_state(
         pbc.load(sp + (int64_t)min(t1 + stok, L - 1) * NS);
         if (astage) pa.load(ap + (int64_t)min(t1 + atok, L - 1) * D);
     };
+    // While the next tile is whole and the previous one was, each thread's rows
+    // advance by one tile per step: running pointers instead of clamped 64-bit
+    // row arithmetic.  spn/apn: this thread's rows of the tile after the
+    // current one; yq: its output row of the previous tile; ckq: its
+    // checkpoint piece of the previous tile.
+    const T* spn = sp + (int64_t)(LT + stok) * NS;
+    const T* apn = ap + (int64_t)(LT + atok) * D;
+    T* yq = yrow + (int64_t)atok * D;
+    float4* ckq = CK ? reinterpret_cast<float4*>(ckpt) +
+                           (((int64_t)(threadIdx.x >> 6) * gridDim.y + b) * 4 + ((threadIdx.x >> 4) & 3)) * D +
+                           cb * 16 + (threadIdx.x & 15)
+                     : nullptr;
+    const int64_t ckstep = (int64_t)(LT / TS) * gridDim.y * 4 * D;
     auto stage_store = [&](int buf, const Pair<T>& pbc, const Quad<T>& pa) {
         bc[buf][st][sn * LRS + stok] = pbc.lo();
         bc[buf][st][(sn + 1) * LRS + stok] = pbc.hi();
@@ -575,13 +588,21 @@ __global__ __launch_bounds__(WG) void k_fwd_state(
         stage_store(0, p0, a0);
     }
     __syncthreads();
-    auto tile = [&](int k, auto full_c) {
+    auto tile = [&](int k, auto full_c, auto next_full_c) {
         constexpr bool FULL = decltype(full_c)::value;
+        constexpr bool NEXT_FULL = decltype(next_full_c)::value;
         const int t0 = k * LT;
         const int buf = k & 1;
         Pair<T> pbc;
         Quad<T> pa;
-        stage_load(t0 + LT, pbc, pa);  // the next tile's loads first
+        if (NEXT_FULL) {  // the next tile's loads first
+            pbc.load(spn);
+            if (astage) pa.load(apn);
+        } else {
+            stage_load(t0 + LT, pbc, pa);
+        }
+        spn += LT * NS;
+        apn += (int64_t)LT * D;
         __builtin_amdgcn_sched_barrier(0);
         float Bv[LT], Cv[LT];
         {
@@ -600,9 +621,17 @@ __global__ __launch_bounds__(WG) void k_fwd_state(
         float sg;
         const float delta = softplus_sig(to_f(act_s[buf][1][n][cw]) + bias, sg);
         const float dxv = delta * xv;
-        if (k > 0) {
-            store_y(buf ^ 1, t0 - LT);
-            store_ck(buf ^ 1, t0 - LT);
+        if (k > 0) {  // the previous tile is whole: all its rows and checkpoints exist
+            if (threadIdx.x < 64) {
+                Quad<T> q;
+                q.load(&y_s[buf ^ 1][atok][a4]);
+                q.store(yq);
+            }
+            if (CK && threadIdx.x < 128) {
+                *ckq = ck_s[buf ^ 1][threadIdx.x >> 6][(threadIdx.x >> 4) & 3][threadIdx.x & 15];
+                ckq += ckstep;
+            }
+            yq += (int64_t)LT * D;
         }
         float yp[LT];
         for_each_i([&](auto ic) {
@@ -645,8 +674,9 @@ __global__ __launch_bounds__(WG) void k_fwd_state(
         __syncthreads();
     };
     const int nfull = L / LT;
-    for (int k = 0; k < nfull; ++k) tile(k, std::true_type{});
-    if (nfull < ntile) tile(nfull, std::false_type{});
+    for (int k = 0; k + 1 < nfull; ++k) tile(k, std::true_type{}, std::true_type{});
+    if (nfull > 0) tile(nfull - 1, std::true_type{}, std::false_type{});
+    if (nfull < ntile) tile(nfull, std::false_type{}, std::false_type{});
     store_y((ntile - 1) & 1, (ntile - 1) * LT);
     store_ck((ntile - 1) & 1, (ntile - 1) * LT);
     if (h_last) h_last[((int64_t)b * D + d) * NS + n] = h;
