@@ -394,13 +394,16 @@ def test_step_row_groups_match_forward(io, gate):
 # Widths from 8192 up to 262143 batch rows x channels (d_inner a multiple of 16)
 # run the forward with one lane per (channel, state) over the whole sequence
 # (k_fwd_state, no chunks, no forward workspace); 2 x 4096 below.
-@pytest.mark.parametrize("L", [1, 17, 1000])
+@pytest.mark.parametrize("L", [1, 16, 17, 32, 48, 1000])
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("gate", [True, False])
 def test_state_lane_forward(L, io, gate):
-    """One-token and ragged sequences (17 = one 16-token tile and one token,
-    1000 = 62 tiles and 8 tokens), with h0; with the gate, D and dt_bias, or
-    with none of them.  The backward reads the checkpoints this forward writes."""
+    """One-token, whole-tile and ragged sequences (16, 32, 48 = one, two, three
+    16-token tiles and no partial one; 17 = one tile and one token; 1000 = 62
+    tiles and 8 tokens), with h0; with the gate, D and dt_bias, or with none of
+    them.  Whole tiles followed by whole tiles advance their row pointers by a
+    tile; the last whole tile and a partial one clamp their rows.  The backward
+    reads the checkpoints this forward writes."""
     assert ssm.fwd_workspace_bytes(2, L, 4096, io_dtype=io) == 0
     inp = W.make_inputs(2, L, 4096, seed=31 + L, bf16=io == torch.bfloat16)
     if not gate:
